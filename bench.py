@@ -1,0 +1,201 @@
+"""Benchmark: one 16384-row prefill chunk at 262144-position context through the
+two-level candidate indexer (source layer + 4 consumer layers) on one MI355X.
+
+A step is one whole chunk: idx_score_dense, then on a side stream
+idx_amax8_varlen / idx_topk_blocks / idx_expand_candidates, the source's own
+top-512, and for each of the 4 consumers idx_score_sparse_paged +
+idx_topk_rows.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line: query-rows/s and ms per chunk, the dense score kernel
+against the fp4 MFMA peak (HIP events on its stream), per-kernel times, and
+the CPU oracle timed on a bounded sample of the same chunk's rows.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexer query-rows/s + ms per 16K-row chunk at 262K context (source+4 consumers)"
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+class Recorder:
+    """Records a torch event on the current stream at each named mark."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.events = {}
+
+    def mark(self, name):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record(self.torch.cuda.current_stream())
+        self.events.setdefault(name, []).append(ev)
+
+    def spans(self, a, b):
+        ea, eb = self.events.get(a, []), self.events.get(b, [])
+        return [x.elapsed_time(y) for x, y in zip(ea, eb)]
+
+
+def workload(name):
+    import workloads
+    if name == "long":
+        return workloads.long_chunk(), "long: 16384 rows x 262144 context (len 245760+i), H=64, kb=2048, 4 consumers, top-512"
+    if name == "prefill":
+        return workloads.prefill(), "prefill: 2048 rows x 65536 context (len 63488+i), H=64, kb=2048, 4 consumers, top-512"
+    if name == "decode":
+        return workloads.decode(), "decode: 64 requests x 1 row, context U[4096,65536], H=64, kb=2048, 4 consumers, top-512"
+    if name == "tiny":
+        return workloads.tiny(), "tiny: 64 rows x 1024 context, H=8, kb=16, 2 consumers, top-32"
+    raise SystemExit(f"unknown config {name}")
+
+
+def algorithmic_work(wl):
+    """Per-launch algorithmic flops / bytes of each kernel for this workload."""
+    import numpy as np
+    lens = wl.lens.astype(np.int64)
+    H = wl.heads
+    nblk = (lens + 7) // 8
+    keyed = nblk > wl.kb
+    n_kept = np.minimum(nblk, wl.kb)
+    valid = np.where(lens > 0, 8 * n_kept - (8 * nblk - lens), 0)
+    flop_per_logit = 2 * H * 128
+    return {
+        "dense_flops": float(flop_per_logit * lens.sum()),
+        "dense_store_bytes": float(4 * lens.sum()),
+        "amax8_bytes": float((32 * (nblk[keyed] - 1) + 4 * nblk[keyed]).sum()),
+        "topk_blocks_bytes": float((4 * nblk[keyed]).sum() + 4 * wl.kb * wl.rows),
+        "sparse_flops": float(flop_per_logit * valid.sum()),
+        "sparse_gather_bytes": float(68 * valid.sum()),
+        "topk_rows_bytes": float(4 * valid.sum() + 4 * wl.kc * wl.rows),
+    }
+
+
+def cpu_baseline(wl, n_rows):
+    """The oracle, as it stands, on n_rows evenly spaced rows of the same chunk."""
+    import numpy as np
+    import oracle
+    rows = np.unique(np.linspace(0, wl.rows - 1, n_rows).astype(np.int64))
+    oracle._load()
+    t0 = time.perf_counter()
+    oracle.run_chunk(wl, row_ids=rows)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(len(rows) / dt, 3), "unit": "query-rows/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(rows)} evenly spaced rows of the same chunk, source + "
+                      f"{len(wl.layers) - 1} consumers (all steps), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "tiny"])
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="rows of the CPU oracle sample (0 = skip the CPU baseline)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the indexer path is built and timed on a single "
+              "MI355X (rows shard across GPUs with no collective inside the path); "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from two_level_top_amd.chunk import Chunk
+
+    torch.cuda.set_device(0)
+    wl, desc = workload(args.config)
+    print(f"[bench] workload ready: {desc}", file=sys.stderr, flush=True)
+    ch = Chunk(wl)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        ch.run()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.warmup} warmup steps done", file=sys.stderr, flush=True)
+
+    rec = Recorder()
+    ch.recorder = rec
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ch.run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ch.recorder = None
+    ms = (t1 - t0) * 1000.0 / args.steps
+    print(f"[bench] {args.steps} timed steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    work = algorithmic_work(wl)
+    ncons = len(ch.cons_top)
+
+    def avg(a, b):
+        s = rec.spans(a, b)
+        return float(np.mean(s)) if s else float("nan")
+
+    t_dense = avg("dense<", "dense>")
+    t_amax = avg("amax8<", "amax8>")
+    t_tkb = avg("amax8>", "topk_blocks>")
+    t_exp = avg("topk_blocks>", "expand>")
+    t_src = avg("source_topk<", "source_topk>")
+    t_sp = [avg(f"sparse{i}<", f"sparse{i}>") for i in range(ncons)]
+    t_tr = [avg(f"sparse{i}>", f"topk_rows{i}>") for i in range(ncons)]
+    dense_tflops = work["dense_flops"] / (t_dense * 1e-3) / 1e12
+    kernels = {
+        "score_dense": {"ms": round(t_dense, 4), "TFLOP/s": round(dense_tflops, 1),
+                        "frac_fp4_peak": round(dense_tflops / PEAK_FP4_TFLOPS, 4)},
+        "amax8_varlen": {"ms": round(t_amax, 4),
+                         "GB/s": round(work["amax8_bytes"] / (t_amax * 1e-3) / 1e9, 1)},
+        "topk_blocks": {"ms": round(t_tkb, 4),
+                        "GB/s": round(work["topk_blocks_bytes"] / (t_tkb * 1e-3) / 1e9, 1)},
+        "expand_candidates": {"ms": round(t_exp, 4)},
+        "source_topk_rows": {"ms": round(t_src, 4)},
+        "score_sparse_paged": {"ms": round(float(np.mean(t_sp)), 4),
+                               "TFLOP/s": round(work["sparse_flops"] / (np.mean(t_sp) * 1e-3) / 1e12, 1),
+                               "gather GB/s": round(work["sparse_gather_bytes"] / (np.mean(t_sp) * 1e-3) / 1e9, 1)},
+        "consumer_topk_rows": {"ms": round(float(np.mean(t_tr)), 4),
+                               "GB/s": round(work["topk_rows_bytes"] / (np.mean(t_tr) * 1e-3) / 1e9, 1)},
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(wl.rows / (ms * 1e-3), 1),
+        "unit": "query-rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": desc, "rows": wl.rows, "heads": wl.heads, "kb": wl.kb,
+                   "topk": wl.kc, "consumers": ncons},
+        "roofline": {"bound": "mfma", "kernel": "score_dense",
+                     "achieved": round(dense_tflops, 2), "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_FP4_TFLOPS, 4),
+                     "traffic": None},
+        "kernels": kernels,
+    }
+    if args.cpu_rows > 0:
+        print(f"[bench] timing the CPU oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,278 @@
+/*
+ * idx.h -- C ABI of the two-level candidate indexer for MI355X (gfx950).
+ *
+ * The method (DeepSeek-V4.1 hierarchical sparse indexer, as described by the
+ * sglang PR "[DSv4.1] Score prefill consumer index layers on candidate blocks
+ * with DeepGEMM", Motivation and Design sections, and the sglang PR "dsv4.1:
+ * candidate indexer library", Summary):
+ *
+ *   source layer   score every reachable compressed position of each query
+ *                  row (idx_score_dense), reduce the scores to one key per
+ *                  block of 8 positions with the newest block forced to +inf
+ *                  (idx_amax8_varlen), keep the kb best blocks, ascending
+ *                  (idx_topk_blocks), expand them to pool blocks and record
+ *                  the ready event (idx_expand_candidates); take its own
+ *                  top-k (idx_topk_rows).
+ *   consumer layer score only the published blocks, straight from the paged
+ *                  index-K pool (idx_score_sparse_paged), and keep its own
+ *                  top-k over them (idx_topk_rows).
+ *   tail           restrict a published table to the last rows of each
+ *                  request (idx_prefill_tail).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer is a device pointer unless its name ends in _host.
+ * - The caller owns every buffer, stream and event.  The library never
+ *   allocates or frees device memory and never synchronises the device
+ *   (one exception: idx_prefill_tail waits for its own small host-to-device
+ *   copy of the tail row list on its stream).
+ * - Every call validates its arguments on the host before enqueuing anything;
+ *   on error it returns a negative idx_status, enqueues nothing, and
+ *   idx_last_error() describes the problem.  Work is asynchronous on the
+ *   given stream (0 = the null stream).
+ * - Preconditions that live in device memory are NOT checked (the contents
+ *   of len/req/page_table/blocks).  They are listed per call.  Out-of-range
+ *   page-table entries are clamped into the pool so that a bad table can
+ *   give wrong scores but never reads outside the pool.
+ * - Index dimension d = 128, pool page = 64 positions, block = 8 positions.
+ *
+ * MXFP4 (the vLLM sparse_attn_indexer page, MXFP4 layout constants): each
+ * 128-element vector is 64 bytes of e2m1 codes, two per byte (element 2i in
+ * the low nibble of byte i), plus 4 ue8m0 scale bytes, one per 32 elements;
+ * value = e2m1(code) * 2^(scale - 127).  Scale byte 255 is outside the
+ * contract.
+ *
+ * Score (the "MQA logits" of the index layer: one key vector per position,
+ * per-(row, head) weights):
+ *     score(r, p) = sum_h w[r,h] * max(0, dot(q[r,h], k[p]))     (fp32)
+ */
+#ifndef IDX_H_
+#define IDX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_E_ARG = -1,         /* null pointer, negative size, bad enum           */
+  IDX_E_ALIGN = -2,       /* pointer or stride misaligned                    */
+  IDX_E_SHAPE = -3,       /* sizes inconsistent with each other              */
+  IDX_E_UNSUPPORTED = -4, /* valid but not implemented (e.g. dim != 128)     */
+  IDX_E_HIP = -5,         /* a HIP runtime call failed                       */
+  IDX_E_WORKSPACE = -6    /* workspace missing or smaller than required      */
+} idx_status;
+
+/* Message of the last failing call on this thread ("" after a success).
+ * Valid until the next idx_* call on the same thread. */
+const char* idx_last_error(void);
+
+/* Library version string, e.g. "idx 0.1 gfx950". */
+const char* idx_version(void);
+
+/* A query batch of one index layer.
+ *   vals   u8  [rows][heads][64]   packed e2m1 codes
+ *   scales u8  [rows][heads][4]    ue8m0 scales
+ *   w      f32 [rows][heads]       head weights (already folded upstream)
+ * 1 <= heads <= 64 (64 in the model; 8 in small tests); dim must be 128. */
+typedef struct {
+  const uint8_t* vals;
+  const uint8_t* scales;
+  const float* w;
+  int32_t rows;
+  int32_t heads;
+  int32_t dim;
+} idx_query;
+
+/* The paged MXFP4 index-K pool (the vLLM sparse_attn_indexer page,
+ * kv_cache_as_quant_view: pages of page_size positions, 68 bytes each).
+ * Byte layout of page g (page_bytes = page_size * 68):
+ *     [0, page_size*64)                 values of slots 0..page_size-1
+ *     [page_size*64, page_size*68)      scales of slots 0..page_size-1
+ * so a block of 8 positions is 512 contiguous value bytes plus 32
+ * contiguous scale bytes.  Position p of request j is slot p % page_size of
+ * page page_table[j * max_pages + p / page_size].
+ *   pool       u8  [num_pages][page_bytes]
+ *   page_table i32 [num_req][max_pages]
+ * page_size must be 64, dim 128.  The pool must be 16-byte aligned. */
+typedef struct {
+  const uint8_t* pool;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t dim;
+  const int32_t* page_table;
+  int32_t num_req;
+  int32_t max_pages;
+} idx_kpool;
+
+/* Per-row metadata of a chunk.
+ *   req        i32 [rows]  request of each row (0 <= req < num_req)
+ *   len        i32 [rows]  compress_len: the row may see positions [0, len)
+ *   pos_offset i32 [rows]  nullable; added to output positions (the request's
+ *                          first flattened-K column turns request-relative
+ *                          positions into flattened-K columns)
+ * Device preconditions (not checked): 0 <= len <= max_pages * page_size. */
+typedef struct {
+  const int32_t* req;
+  const int32_t* len;
+  const int32_t* pos_offset;
+  int32_t rows;
+} idx_rows;
+
+/* A published candidate table (the PR's PrefillSparseBlockTable): one row per
+ * query row, all buffers caller-owned.
+ *   blocks    i32 [rows][kb]  kept block ids, ascending, INT32_MAX padded
+ *   n_kept    i32 [rows]      number of kept blocks = min(nblk, kb)
+ *   phys      i32 [rows][kb]  pool block of each kept block:
+ *                             page * 8 + block-in-page, -1 padded
+ *   valid_len i32 [rows]      number of candidate columns below len: column c
+ *                             is position blocks[c/8]*8 + c%8, c < valid_len
+ *   len, req  i32 [rows]      copies of the rows it was built from
+ *   schedule  u8  [schedule_bytes]  work list of the sparse scorer
+ *                             (idx_workspace_bytes(IDX_OP_SCHEDULE, rows, kb, 0))
+ *   ready     event recorded when the table is complete (nullable). */
+typedef struct {
+  int32_t* blocks;
+  int32_t* n_kept;
+  int32_t* phys;
+  int32_t* valid_len;
+  int32_t* len;
+  int32_t* req;
+  void* schedule;
+  size_t schedule_bytes;
+  int32_t rows;
+  int32_t kb;
+  hipEvent_t ready;
+} idx_table;
+
+/* Workspace sizes (bytes) for the calls that take one. */
+enum {
+  IDX_OP_TOPK_BLOCKS = 1, /* idx_topk_blocks: rows, width = ldk, k = kb     */
+  IDX_OP_TOPK_ROWS = 2,   /* idx_topk_rows:   rows, width = columns, k      */
+  IDX_OP_SCHEDULE = 3,    /* idx_table.schedule: rows, width = kb           */
+  IDX_OP_TAIL = 4         /* idx_prefill_tail: rows = tail rows             */
+};
+size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k);
+
+/*
+ * idx_score_dense -- the source layer's dense scores.
+ * Prefill PR, Motivation: the fp32 [tokens, context] score matrix that the
+ * source scores in full; vLLM indexer page: fp8_fp4_mqa_logits over
+ * [ks, ke) of each row.
+ *   S[r * ld + p] = score(r, p) for p < len[r]; S beyond len[r] is not written.
+ * q->rows == rows->rows; ld >= max len (not checked: device data) and ld >= 1;
+ * S must be 4-byte aligned.
+ */
+idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows,
+                           float* S, int64_t ld, hipStream_t stream);
+
+/*
+ * idx_amax8_varlen -- block keys (the block_amax.cuh contract quoted in the
+ * prefill PR's review thread, and "Level one" of its Design):
+ *   keys[r * ldk + i] = max(S[r*ld + 8i .. 8i+7]) for i < nblk - 1,
+ *   keys[r * ldk + nblk - 1] = +inf,          nblk = ceil(len[r] / 8);
+ *   rows with nblk <= skip_le_blocks are left untouched (0 = never skip).
+ * ld % 8 == 0 and S 32-byte aligned (every block is one 32-byte load).
+ * Device precondition: nblk <= ldk for every row.  NaN scores are ignored by
+ * the max (outside the contract).
+ */
+idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int32_t rows,
+                            float* keys, int64_t ldk, int32_t skip_le_blocks, hipStream_t stream);
+
+/*
+ * idx_topk_blocks -- the kb best blocks of each row (prefill PR, "Level one":
+ * ragged top-k over the keys, trivial path for rows with at most kb blocks,
+ * sort_candidate_blocks' ascending INT32_MAX-padded order).
+ *   if nblk <= kb: blocks = 0 .. nblk-1
+ *   else: the kb largest keys, ties to the lower block id
+ *   blocks[r * kb ..] ascending, INT32_MAX padded; n_kept[r] = min(nblk, kb).
+ * ws: idx_workspace_bytes(IDX_OP_TOPK_BLOCKS, rows, ldk, kb) bytes (may be 0).
+ */
+idx_status idx_topk_blocks(const float* keys, int64_t ldk, const int32_t* len, int32_t rows,
+                           int32_t kb, int32_t* blocks, int32_t* n_kept, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/*
+ * idx_expand_candidates -- pool blocks, valid lengths and the sparse work list
+ * of a table whose blocks/n_kept were written by idx_topk_blocks (prefill PR,
+ * "Level one": pool slots and the schedule; vLLM decode page:
+ * candidate_blocks_to_sparse_indices + the sparse logits schedule).  Copies
+ * rows->len and rows->req into the table, then records tbl->ready on stream.
+ *   phys[r*kb + i] = page_table[req[r]][blocks[r*kb+i] / 8] * 8 + blocks % 8
+ *   valid_len[r]   = 8 * n_kept[r] - (8 * nblk - len[r])   (0 when len = 0)
+ * tbl->rows == rows->rows; tbl->schedule_bytes >= the IDX_OP_SCHEDULE size.
+ */
+idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_table* tbl,
+                                 hipStream_t stream);
+
+/*
+ * idx_score_sparse_paged -- a consumer's scores at its candidate positions
+ * only (prefill PR, "Level two": scores written [tokens, kb*8] in ascending
+ * block order, read straight from the paged pool).  Makes `stream` wait on
+ * tbl->ready first (if set).
+ *   T[r * ld + c] = score'(r, blocks[r][c/8]*8 + c%8) for c < valid_len[r];
+ *   T beyond valid_len[r] is not written.
+ * q->rows == tbl->rows; ld >= tbl->kb * 8.
+ */
+idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
+                                  float* T, int64_t ld, hipStream_t stream);
+
+/* Column modes of idx_topk_rows. */
+enum {
+  IDX_COLS_IDENTITY = 0,  /* column c is position c, value X[c]                   */
+  IDX_COLS_BLOCKMAP = 1,  /* column c is position blocks[c/8]*8 + c%8, value X[c]
+                             (a consumer's compact scores, "Level two")           */
+  IDX_COLS_GATHER = 2     /* column c is position blocks[c/8]*8 + c%8 and its
+                             value is read at X[position] (dense scores seen
+                             through the candidate blocks)                         */
+};
+
+/*
+ * idx_topk_rows -- top-k of each row over its first valid[r] columns, ties to
+ * the lower column (= lower position: the column map is increasing), mapped
+ * to positions, plus pos_offset[r] when given, ascending, -1 past
+ * min(k, valid[r]) (prefill PR, "Level two": top-k of the first valid_len
+ * columns with the page transform, -1 past min(512, valid_len); the source's
+ * own top-512 of "The interface").
+ *   out i32 [rows][k]
+ * blocks: i32 [rows][kb], required for BLOCKMAP and GATHER (then valid[r] <=
+ * kb*8 must hold), ignored for IDENTITY.  ld >= valid (IDENTITY, BLOCKMAP) or
+ * ld > every gathered position (GATHER); not checked (device data).
+ * ws: idx_workspace_bytes(IDX_OP_TOPK_ROWS, rows, width, k) bytes (may be 0).
+ * With mode GATHER over a source's own candidate table this equals the dense
+ * top-k of its score rows whenever kb >= k + 1 (every block that holds one of
+ * the k best positions has at most k - 1 other blocks above it).
+ */
+idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32_t rows,
+                         int32_t k, int mode, const int32_t* blocks, int32_t kb,
+                         const int32_t* pos_offset, int32_t* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * idx_prefill_tail -- restrict a published table to the last tail_len[j] rows
+ * of each request j (prefill PR, "Tail rows" and its prefill_tail; the table
+ * keeps its rows' len/req so the work list can be rebuilt for the tail rows).
+ * Request j owns rows [start_j, start_j + rows_per_req[j]) of `full`, starts
+ * being the running sum.  tail->rows must equal sum_j tail_len[j]; tail->kb ==
+ * full->kb.  Waits on full->ready, copies the rows, rebuilds tail->schedule
+ * and records tail->ready.
+ *   rows_per_req_host, tail_len_host: host arrays of num_req entries,
+ *   0 <= tail_len[j] <= rows_per_req[j], sum rows_per_req == full->rows.
+ * ws: idx_workspace_bytes(IDX_OP_TAIL, tail->rows, 0, 0) device bytes; the
+ * host row list is copied into it, and the call synchronises `stream` so the
+ * host copy source can be released before it returns.
+ */
+idx_status idx_prefill_tail(const idx_table* full, const int32_t* rows_per_req_host,
+                            const int32_t* tail_len_host, int32_t num_req, idx_table* tail,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H_ */

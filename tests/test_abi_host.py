@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI: the library loads, exports every call that
+include/idx.h declares, and rejects bad arguments before touching the GPU."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idx.h")
+LIB = os.path.join(ROOT, "two_level_top_amd", "libidx.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libidx.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_seven_calls():
+    names = declared_functions()
+    for n in ("idx_score_dense", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
+              "idx_score_sparse_paged", "idx_topk_rows", "idx_prefill_tail"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_no_torch_types_in_the_abi():
+    text = open(HEADER).read()
+    assert "torch" not in text.lower().replace("pytorch", "")
+    assert "at::" not in text and "c10" not in text
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import two_level_top_amd as t
+    return t.load()
+
+
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x100004)
+
+
+def _err(lib):
+    return lib.idx_last_error().decode()
+
+
+def test_amax8_validation(lib):
+    assert lib.idx_amax8_varlen(FAKE, 12, FAKE, 4, FAKE, 4, 0, None) == -2     # ld % 8
+    assert "multiple of 8" in _err(lib)
+    assert lib.idx_amax8_varlen(FAKE_ODD, 16, FAKE, 4, FAKE, 4, 0, None) == -2  # 32-byte alignment
+    assert lib.idx_amax8_varlen(None, 16, FAKE, 4, FAKE, 4, 0, None) == -1
+    assert lib.idx_amax8_varlen(FAKE, 16, FAKE, -1, FAKE, 4, 0, None) == -1
+    assert lib.idx_amax8_varlen(FAKE, 16, FAKE, 4, FAKE, 0, 0, None) == -1     # ldk < 1
+    assert lib.idx_amax8_varlen(FAKE, 16, FAKE, 0, FAKE, 4, 0, None) == 0       # nothing to do
+    assert _err(lib) == ""
+
+
+def test_topk_validation(lib):
+    assert lib.idx_topk_blocks(FAKE, 4, FAKE, 2, 0, FAKE, FAKE, None, 0, None) == -1   # kb < 1
+    assert lib.idx_topk_rows(FAKE, 8, FAKE, 2, 0, 0, None, 0, None, FAKE, None, 0, None) == -1  # k < 1
+    assert lib.idx_topk_rows(FAKE, 8, FAKE, 2, 4, 7, None, 0, None, FAKE, None, 0, None) == -1  # mode
+    assert lib.idx_topk_rows(FAKE, 8, FAKE, 2, 4, 1, None, 4, None, FAKE, None, 0, None) == -1  # no blocks
+    assert lib.idx_topk_rows(FAKE, 8, FAKE, 2, 4, 1, FAKE, 4, None, FAKE, None, 0, None) == -3  # ld < kb*8
+
+
+def _structs():
+    import two_level_top_amd as t
+    q = t._Query(FAKE, FAKE, FAKE, 4, 64, 128)
+    kp = t._KPool(FAKE, 16, 64, 128, FAKE, 1, 16)
+    rows = t._Rows(FAKE, FAKE, None, 4)
+    tbl = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 4, 16, None)
+    return t, q, kp, rows, tbl
+
+
+def test_score_validation(lib):
+    t, q, kp, rows, tbl = _structs()
+    P = ctypes.byref
+    bad = t._Query(FAKE, FAKE, FAKE, 4, 64, 64)
+    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, None) == -4        # dim
+    bad = t._Query(FAKE, FAKE, FAKE, 4, 65, 128)
+    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, None) == -4        # heads
+    bad = t._Query(FAKE_ODD, FAKE, FAKE, 4, 64, 128)
+    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, None) == -2        # alignment
+    badkp = t._KPool(FAKE, 16, 32, 128, FAKE, 1, 16)
+    assert lib.idx_score_dense(P(q), P(badkp), P(rows), FAKE, 1024, None) == -4       # page size
+    r3 = t._Rows(FAKE, FAKE, None, 3)
+    assert lib.idx_score_dense(P(q), P(kp), P(r3), FAKE, 1024, None) == -3            # rows mismatch
+    assert lib.idx_score_dense(None, P(kp), P(rows), FAKE, 1024, None) == -1
+    small = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 16, None)
+    assert lib.idx_score_sparse_paged(P(q), P(kp), P(small), FAKE, 128, None) == -6   # schedule size
+    assert lib.idx_score_sparse_paged(P(q), P(kp), P(tbl), FAKE, 64, None) == -3      # ld < kb*8
+    assert lib.idx_expand_candidates(P(kp), P(r3), P(tbl), None) == -3
+
+
+def test_tail_validation(lib):
+    t, q, kp, rows, tbl = _structs()
+    P = ctypes.byref
+    rpr = (ctypes.c_int32 * 2)(3, 1)
+    tl = (ctypes.c_int32 * 2)(2, 2)       # tail longer than its request
+    tail = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 4, 16, None)
+    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail), FAKE, 64, None) == -1
+    tl = (ctypes.c_int32 * 2)(2, 1)
+    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail), FAKE, 64, None) == -3    # 3 tail rows != 4
+    tail3 = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 3, 16, None)
+    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail3), FAKE, 4, None) == -6    # workspace
+    rpr = (ctypes.c_int32 * 2)(2, 1)
+    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail3), FAKE, 64, None) == -3   # 3 rows != 4
+
+
+def test_workspace_sizes(lib):
+    assert lib.idx_workspace_bytes(3, 16384, 2048, 0) == 16 + 16384 * 32 * 8
+    assert lib.idx_workspace_bytes(4, 100, 0, 0) == 400
+    assert lib.idx_workspace_bytes(1, 100, 32768, 2048) == 0

@@ -1,0 +1,403 @@
+"""GPU parity of the HIP path against the CPU oracle, call by call and end to end.
+
+Selection steps (block keys, block selection, expansion, top-k) do no float
+arithmetic beyond comparisons: they are checked bit for bit on inputs the
+oracle also sees.  Score steps are checked within |gpu - oracle| <=
+1e-4 + 1e-5 * |oracle|.  Where a selection consumes GPU scores, sets may
+differ only at ties within that tolerance of the k-th value.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-4, 1e-5
+INT32_MAX = np.iinfo(np.int32).max
+
+
+def say(msg: str):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def idx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import two_level_top_amd as t
+    t.load()
+    return t
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return t if dtype is None else t.to(dtype)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_close(gpu, ora, mask, what):
+    g, o = gpu[mask].astype(np.float64), ora[mask].astype(np.float64)
+    assert np.isfinite(g).all(), f"{what}: non-finite GPU values"
+    err = np.abs(g - o)
+    bound = ATOL + RTOL * np.abs(o)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside tolerance, worst {err.max():.3g}"
+
+
+def within_tol(a, b):
+    return abs(float(a) - float(b)) <= ATOL + RTOL * abs(float(b))
+
+
+def assert_same_selection(gpu_row, ora_row, score_of, kth, pad, what):
+    """Equal sets, or differences only at ties within tolerance of the k-th value."""
+    g = set(int(x) for x in gpu_row if x != pad)
+    o = set(int(x) for x in ora_row if x != pad)
+    assert len(g) == len(o), f"{what}: {len(g)} vs {len(o)} picks"
+    for x in g ^ o:
+        s = score_of(x)
+        assert s is not None and within_tol(s, kth), f"{what}: pick {x} score {s} vs k-th {kth}"
+    assert list(gpu_row) == sorted(gpu_row, key=lambda v: (v == pad, v)), f"{what}: not ascending"
+
+
+def kth_largest(vals, k):
+    v = np.sort(vals.astype(np.float64))[::-1]
+    return v[min(k, len(v)) - 1]
+
+
+# ---------------------------------------------------------------------------
+# idx_score_dense
+# ---------------------------------------------------------------------------
+
+def _dense_gpu(idx, wl, layer_i, ld=None):
+    from two_level_top_amd.chunk import Chunk
+    ch = Chunk(wl, n_consumers=0)
+    L = wl.layers[layer_i]
+    q = idx.Query(dev(L.qv), dev(L.qs), dev(L.w))
+    S = torch.full((wl.rows, ld or wl.ld), float("nan"), dtype=torch.float32, device="cuda")
+    idx.idx_score_dense(q, ch.kp, ch.rows, S)
+    return host(S)
+
+
+def _check_dense(idx, wl, layer_i, rows=None):
+    S = _dense_gpu(idx, wl, layer_i)
+    L = wl.layers[layer_i]
+    rows = np.arange(wl.rows) if rows is None else np.asarray(rows)
+    ref = oracle.dense_scores(L.qv, L.qs, L.w, wl.req, wl.lens, wl.pool, wl.page_table,
+                              row_ids=rows, ld=wl.ld)
+    valid = np.arange(wl.ld)[None, :] < wl.lens[rows][:, None]
+    assert_close(S[rows], ref, valid, f"{wl.name} layer {layer_i} dense")
+    # nothing written past each row's length
+    assert np.isnan(S[rows][~valid]).all(), "dense scores written past len"
+
+
+def test_dense_tiny(idx):
+    wl = workloads.tiny()
+    for i in range(3):
+        say(f"dense tiny layer {i}")
+        _check_dense(idx, wl, i)
+
+
+@pytest.mark.parametrize("heads", [64, 8, 24])
+def test_dense_ragged_requests(idx, heads):
+    # ragged lengths, an empty row, pairs of rows from different requests,
+    # contexts that are not multiples of a tile or page
+    wl = workloads.custom("ragged", 31 + heads, heads, 4, 8, [1000, 77, 5, 300, 2100],
+                          [5, 1, 2, 3, 4],
+                          [[990, 996, 997, 998, 1000], [77], [0, 5], [1, 250, 300], [1, 64, 1500, 2100]],
+                          n_layers=1)
+    say(f"dense ragged heads={heads}")
+    _check_dense(idx, wl, 0)
+
+
+def test_dense_prefill_sampled(idx):
+    wl = workloads.prefill(n_consumers=0)
+    say("dense prefill 2048 x 65536 (sampled rows)")
+    _check_dense(idx, wl, 0, rows=[0, 1, 2, 777, 1024, 2045, 2046, 2047])
+
+
+# ---------------------------------------------------------------------------
+# idx_amax8_varlen (bit-exact on synthetic scores)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("width,kb", [(2048, 16), (65536, 2048), (262144, 2048)])
+def test_amax8_bitexact(idx, width, kb):
+    rows = 64 if width <= 65536 else 24
+    S = workloads.random_matrix(width, rows, width)
+    lens = workloads.random_lengths(width, rows, 0, width,
+                                    extra=[0, 1, 7, 8, 9, width, width - 1, 8 * kb, 8 * kb + 1, 8 * kb - 1])
+    nblk = oracle.nblocks(lens)
+    ldk = width // 8
+    say(f"amax8 width={width} kb={kb}")
+    keys_g = torch.full((rows, ldk), -7.0, dtype=torch.float32, device="cuda")
+    idx.idx_amax8_varlen(dev(S), dev(lens), keys_g, skip_le_blocks=kb)
+    kg = host(keys_g)
+    ko = oracle.block_keys(S, lens, kb, ldk=ldk)
+    for r in range(rows):
+        m = int(nblk[r])
+        if m <= kb:
+            assert (kg[r] == -7.0).all(), f"row {r} (nblk {m} <= kb) was written"
+        else:
+            # equal fp32 values (+0 and -0 are the same key)
+            assert np.array_equal(kg[r, :m], ko[r, :m]), f"row {r}"
+            assert (kg[r, m:] == -7.0).all(), f"row {r} written past nblk"
+
+
+# ---------------------------------------------------------------------------
+# idx_topk_blocks (bit-exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kb,maxblk", [(16, 128), (2048, 32768), (2048, 8192), (3, 40)])
+def test_topk_blocks_bitexact(idx, kb, maxblk):
+    rows = 48
+    keys = workloads.random_matrix(kb + maxblk, rows, maxblk)
+    nb = workloads.random_lengths(kb + maxblk, rows, 0, maxblk,
+                                  extra=[0, 1, kb - 1, kb, kb + 1, 2 * kb, maxblk, maxblk - 1])
+    lens = (nb * 8 - (np.arange(rows) % 8)).clip(0).astype(np.int32)   # ragged newest blocks
+    nblk = oracle.nblocks(lens)
+    for r in range(rows):                # a keyed row's newest block is +inf
+        if nblk[r] > 0:
+            keys[r, nblk[r] - 1] = np.inf
+    say(f"topk_blocks kb={kb} maxblk={maxblk}")
+    blocks = torch.full((rows, kb), -5, dtype=torch.int32, device="cuda")
+    n_kept = torch.full((rows,), -5, dtype=torch.int32, device="cuda")
+    idx.idx_topk_blocks(dev(keys), dev(lens), kb, blocks, n_kept)
+    bo, no = oracle.select_blocks(keys, lens, kb)
+    assert np.array_equal(host(n_kept), no)
+    assert np.array_equal(host(blocks), bo)
+
+
+# ---------------------------------------------------------------------------
+# idx_topk_rows (bit-exact, three column modes)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("width,k", [(16384, 512), (1024, 32), (70000, 512), (300, 512)])
+def test_topk_rows_identity(idx, width, k):
+    rows = 32
+    X = workloads.random_matrix(7 * width + k, rows, width)
+    extra = [v for v in (0, 1, k - 1, k, k + 1, width) if v <= width]
+    valid = workloads.random_lengths(width + k, rows, 0, width, extra=extra)
+    off = np.arange(rows, dtype=np.int32) * 1000
+    say(f"topk_rows identity width={width} k={k}")
+    out = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows(dev(X), dev(valid), k, out, mode=idx.COLS_IDENTITY, pos_offset=dev(off))
+    ref = oracle.topk_positions(X, valid, k, pos_offset=off)
+    assert np.array_equal(host(out), ref)
+
+
+def _random_blocks(seed, rows, kb, nblk_max):
+    r = np.random.default_rng(seed)
+    blocks = np.full((rows, kb), INT32_MAX, np.int32)
+    nk = np.zeros(rows, np.int32)
+    for i in range(rows):
+        n = int(r.integers(0, kb + 1)) if i % 3 else kb
+        b = np.sort(r.choice(nblk_max, size=n, replace=False)).astype(np.int32)
+        blocks[i, :n] = b
+        nk[i] = n
+    return blocks, nk
+
+
+@pytest.mark.parametrize("kb,k", [(2048, 512), (16, 32), (64, 8)])
+def test_topk_rows_blockmap_and_gather(idx, kb, k):
+    rows = 24
+    nblk_max = 4 * kb + 5
+    blocks, nk = _random_blocks(kb, rows, kb, nblk_max)
+    valid = np.maximum(nk * 8 - (np.arange(rows) % 8), 0).astype(np.int32)
+    valid[nk == 0] = 0
+    T = workloads.random_matrix(kb + k, rows, kb * 8)
+    dense = workloads.random_matrix(kb + k + 1, rows, nblk_max * 8)
+    off = (np.arange(rows, dtype=np.int32) * 7).astype(np.int32)
+    pos = oracle.candidate_positions(blocks, valid)
+    say(f"topk_rows blockmap kb={kb} k={k}")
+    out = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows(dev(T), dev(valid), k, out, mode=idx.COLS_BLOCKMAP, blocks=dev(blocks),
+                      pos_offset=dev(off))
+    ref = oracle.topk_positions(T, valid, k, colmap=pos, pos_offset=off)
+    assert np.array_equal(host(out), ref)
+    say(f"topk_rows gather kb={kb} k={k}")
+    out2 = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows(dev(dense), dev(valid), k, out2, mode=idx.COLS_GATHER, blocks=dev(blocks))
+    gathered = np.take_along_axis(dense, np.maximum(pos, 0).astype(np.int64), 1)
+    ref2 = oracle.topk_positions(gathered, valid, k, colmap=pos)
+    assert np.array_equal(host(out2), ref2)
+
+
+# ---------------------------------------------------------------------------
+# idx_expand_candidates + idx_score_sparse_paged
+# ---------------------------------------------------------------------------
+
+def _table_from_oracle(idx, ch, blocks, n_kept):
+    ch.table.blocks.copy_(dev(blocks))
+    ch.table.n_kept.copy_(dev(n_kept))
+    idx.idx_expand_candidates(ch.kp, ch.rows, ch.table)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_expand_and_sparse_scores(idx, name):
+    from two_level_top_amd.chunk import Chunk
+    wl = workloads.tiny() if name == "tiny" else workloads.decode(n_consumers=1)
+    rows = np.arange(wl.rows)
+    # candidate blocks from the oracle's own source scores
+    L0 = wl.layers[0]
+    S = oracle.dense_scores(L0.qv, L0.qs, L0.w, wl.req, wl.lens, wl.pool, wl.page_table,
+                            row_ids=rows if name == "tiny" else rows[:8], ld=wl.ld)
+    sub = rows if name == "tiny" else rows[:8]
+    keys = oracle.block_keys(S, wl.lens[sub], wl.kb, ldk=wl.ldk)
+    b_sub, n_sub = oracle.select_blocks(keys, wl.lens[sub], wl.kb)
+    # rows outside the sample get keep-all or random ascending blocks
+    blocks = np.full((wl.rows, wl.kb), INT32_MAX, np.int32)
+    n_kept = np.zeros(wl.rows, np.int32)
+    blocks[sub], n_kept[sub] = b_sub, n_sub
+    rest = np.setdiff1d(rows, sub)
+    if len(rest):
+        k_rest = np.full((len(rest), wl.ldk), 0.0, np.float32)
+        nb_rest = oracle.nblocks(wl.lens[rest])
+        k_rest[np.arange(len(rest)), np.maximum(nb_rest - 1, 0)] = np.inf   # newest block kept
+        b_r, n_r = oracle.select_blocks(k_rest, wl.lens[rest], wl.kb)
+        blocks[rest], n_kept[rest] = b_r, n_r
+    say(f"expand {name}")
+    ch = Chunk(wl, n_consumers=1)
+    _table_from_oracle(idx, ch, blocks, n_kept)
+    phys_o, valid_o = oracle.expand(blocks, n_kept, wl.lens, wl.req, wl.page_table)
+    assert np.array_equal(host(ch.table.phys), phys_o)
+    assert np.array_equal(host(ch.table.valid_len), valid_o)
+    assert np.array_equal(host(ch.table.len), wl.lens)
+    assert np.array_equal(host(ch.table.req), wl.req)
+    sched = host(ch.table.schedule).view(np.int32)
+    units = (n_kept + 63) // 64
+    assert sched[0] == units.sum()
+    pairs = sched[4:4 + 2 * sched[0]].reshape(-1, 2)
+    exp = np.array([(r, 64 * u) for r in range(wl.rows) for u in range(units[r])]).reshape(-1, 2)
+    assert np.array_equal(pairs, exp)
+    say(f"sparse scores {name}")
+    L1 = wl.layers[1]
+    T = torch.full((wl.rows, wl.kb * 8), float("nan"), dtype=torch.float32, device="cuda")
+    idx.idx_score_sparse_paged(ch.queries[1], ch.kp, ch.table, T)
+    Tg = host(T)
+    pos = oracle.candidate_positions(blocks, valid_o)
+    check = rows if name == "tiny" else rows[::4]
+    To = oracle.scores_at(L1.qv, L1.qs, L1.w, wl.req, pos[check], wl.pool, wl.page_table, row_ids=check)
+    m = pos[check] >= 0
+    assert_close(Tg[check], To, m, f"{name} sparse scores")
+    assert np.isnan(Tg[check][~m]).all(), "sparse scores written past valid_len"
+
+
+# ---------------------------------------------------------------------------
+# the whole chunk
+# ---------------------------------------------------------------------------
+
+def _run_chunk(idx, wl, n_consumers=None):
+    from two_level_top_amd.chunk import Chunk
+    ch = Chunk(wl, n_consumers=n_consumers)
+    ch.run()
+    torch.cuda.synchronize()
+    return ch
+
+
+def _check_chunk(wl, ch, rows, n_consumers):
+    res = oracle.run_chunk(wl, row_ids=rows, n_consumers=n_consumers)
+    Sg = host(ch.S)[rows]
+    valid = np.arange(wl.ld)[None, :] < wl.lens[rows][:, None]
+    assert_close(Sg, res["S"], valid, f"{wl.name} chunk dense")
+    blocks_g = host(ch.table.blocks)[rows]
+    n_kept_g = host(ch.table.n_kept)[rows]
+    valid_g = host(ch.table.valid_len)[rows]
+    src_g = host(ch.src_top)[rows]
+    cons_g = [host(t)[rows] for t in ch.cons_top]
+    same_blocks = 0
+    for i, r in enumerate(rows):
+        L, nb = int(wl.lens[r]), int(oracle.nblocks(wl.lens[r:r + 1])[0])
+        assert n_kept_g[i] == res["n_kept"][i]
+        if nb > wl.kb:
+            kth = kth_largest(res["keys"][i, :nb], wl.kb)
+            assert_same_selection(blocks_g[i], res["blocks"][i], lambda b: res["keys"][i, b], kth,
+                                  INT32_MAX, f"{wl.name} row {r} blocks")
+        else:
+            assert np.array_equal(blocks_g[i], res["blocks"][i])
+        # the source's own top-k: scores are the oracle's dense row
+        row_s = res["S"][i, :L]
+        if L:
+            kth = kth_largest(row_s, ch.k_src)
+            off = int(wl.req_start[r])
+            assert_same_selection(src_g[i], res["source_topk"][i],
+                                  lambda p: row_s[p - off] if 0 <= p - off < L else None, kth, -1,
+                                  f"{wl.name} row {r} source top-k")
+        if np.array_equal(blocks_g[i], res["blocks"][i]):
+            same_blocks += 1
+            assert valid_g[i] == res["valid_len"][i]
+            off = int(wl.req_start[r])
+            for c in range(len(cons_g)):
+                T_o = res["T"][c][i, :valid_g[i]]
+                pos = res["positions"][i, :valid_g[i]]
+                score = dict(zip((pos + off).tolist(), T_o.tolist()))
+                if valid_g[i]:
+                    kth = kth_largest(T_o, wl.kc)
+                    assert_same_selection(cons_g[c][i], res["consumer_topk"][c][i], score.get, kth, -1,
+                                          f"{wl.name} row {r} consumer {c}")
+    assert same_blocks >= 0.9 * len(rows), f"only {same_blocks}/{len(rows)} rows kept identical blocks"
+
+
+def test_chunk_tiny(idx):
+    wl = workloads.tiny()
+    say("chunk tiny")
+    ch = _run_chunk(idx, wl)
+    _check_chunk(wl, ch, np.arange(wl.rows), None)
+
+
+def test_chunk_decode(idx):
+    wl = workloads.decode(n_consumers=2)
+    say("chunk decode (64 requests x 1 row)")
+    ch = _run_chunk(idx, wl)
+    _check_chunk(wl, ch, np.arange(0, 64, 4), None)
+
+
+def test_chunk_mixed_small(idx):
+    wl = workloads.mixed(n_consumers=1, decode_rows=32, max_decode_ctx=65536)
+    say(f"chunk mixed (rows {wl.rows})")
+    ch = _run_chunk(idx, wl)
+    starts = np.concatenate([[0], np.cumsum(wl.rows_per_req)])
+    rows = np.unique(np.concatenate([starts[:-1], starts[1:] - 1, np.arange(0, wl.rows, 397)]))
+    rows = rows[rows < wl.rows]
+    _check_chunk(wl, ch, rows, None)
+
+
+def test_prefill_tail(idx):
+    import two_level_top_amd as t
+    wl = workloads.custom("tail", 7, 16, 4, 6, [300, 200, 90, 64], [40, 3, 1, 5],
+                          [[260 + i for i in range(40)], [197, 198, 199], [90], [60, 61, 62, 63, 64]],
+                          n_layers=2, tail=[5, 3, 1, 0])
+    say("prefill tail")
+    ch = _run_chunk(idx, wl)
+    trows = oracle.tail_rows(wl.rows_per_req, wl.tail_len)
+    tail = t.Table(len(trows), wl.kb)
+    t.idx_prefill_tail(ch.table, wl.rows_per_req, wl.tail_len, tail)
+    for name in ("blocks", "n_kept", "phys", "valid_len", "len", "req"):
+        assert np.array_equal(host(getattr(tail, name)), host(getattr(ch.table, name))[trows]), name
+    # consumer selection on the tail table = the full table's selection of those rows
+    T = torch.full((len(trows), wl.kb * 8), float("nan"), dtype=torch.float32, device="cuda")
+    L = wl.layers[1]
+    q = t.Query(dev(L.qv[trows]), dev(L.qs[trows]), dev(L.w[trows]))
+    t.idx_score_sparse_paged(q, ch.kp, tail, T)
+    out = torch.empty((len(trows), wl.kc), dtype=torch.int32, device="cuda")
+    t.idx_topk_rows(T, tail.valid_len, wl.kc, out, mode=t.COLS_BLOCKMAP, blocks=tail.blocks,
+                    pos_offset=dev(wl.req_start[trows]))
+    assert np.array_equal(host(out), host(ch.cons_top[0])[trows])
+    sched = host(tail.schedule).view(np.int32)
+    assert sched[0] == ((host(tail.n_kept) + 63) // 64).sum()
+
+
+def test_chunk_prefill_sampled(idx):
+    wl = workloads.prefill(n_consumers=2)
+    say("chunk prefill 2048 x 65536 (sampled rows)")
+    ch = _run_chunk(idx, wl)
+    _check_chunk(wl, ch, np.array([0, 5, 1000, 2047]), 2)

@@ -1,0 +1,320 @@
+"""Python binding of libidx, the gfx950 two-level candidate indexer.
+
+Argument marshalling only: torch tensors in, raw device pointers and the
+current HIP stream out to the C ABI of include/idx.h.  Every step runs in the
+library's HIP kernels; there is no fallback.  If libidx.so has not been built
+(``python -c "import __graft_entry__ as g; g.build()"``), every call raises.
+
+Names follow the C ABI: idx_score_dense, idx_amax8_varlen, idx_topk_blocks,
+idx_expand_candidates, idx_score_sparse_paged, idx_topk_rows,
+idx_prefill_tail.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "IdxError", "Query", "KPool", "Rows", "Table", "load",
+    "idx_score_dense", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
+    "idx_score_sparse_paged", "idx_topk_rows", "idx_prefill_tail", "idx_workspace_bytes",
+    "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libidx.so")
+
+COLS_IDENTITY, COLS_BLOCKMAP, COLS_GATHER = 0, 1, 2
+OP_TOPK_BLOCKS, OP_TOPK_ROWS, OP_SCHEDULE, OP_TAIL = 1, 2, 3, 4
+INT32_MAX = 2 ** 31 - 1
+
+
+class IdxError(RuntimeError):
+    pass
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+class _Query(ctypes.Structure):
+    _fields_ = [("vals", _P), ("scales", _P), ("w", _P), ("rows", _I32), ("heads", _I32),
+                ("dim", _I32)]
+
+
+class _KPool(ctypes.Structure):
+    _fields_ = [("pool", _P), ("num_pages", _I32), ("page_size", _I32), ("dim", _I32),
+                ("page_table", _P), ("num_req", _I32), ("max_pages", _I32)]
+
+
+class _Rows(ctypes.Structure):
+    _fields_ = [("req", _P), ("len", _P), ("pos_offset", _P), ("rows", _I32)]
+
+
+class _Table(ctypes.Structure):
+    _fields_ = [("blocks", _P), ("n_kept", _P), ("phys", _P), ("valid_len", _P), ("len", _P),
+                ("req", _P), ("schedule", _P), ("schedule_bytes", ctypes.c_size_t),
+                ("rows", _I32), ("kb", _I32), ("ready", _P)]
+
+
+_lib = None
+_hip = None
+
+
+def load():
+    """Load libidx.so (and the HIP runtime for events); raise if it is not built."""
+    global _lib, _hip
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise IdxError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int
+    sig = {
+        "idx_score_dense": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P],
+        "idx_amax8_varlen": [_P, _I64, _P, _I32, _P, _I64, _I32, _P],
+        "idx_topk_blocks": [_P, _I64, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+        "idx_expand_candidates": [ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), ctypes.POINTER(_Table), _P],
+        "idx_score_sparse_paged": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P],
+        "idx_topk_rows": [_P, _I64, _P, _I32, _I32, ctypes.c_int, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+        "idx_prefill_tail": [ctypes.POINTER(_Table), _P, _P, _I32, ctypes.POINTER(_Table), _P, ctypes.c_size_t, _P],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = st
+    lib.idx_last_error.restype = ctypes.c_char_p
+    lib.idx_last_error.argtypes = []
+    lib.idx_version.restype = ctypes.c_char_p
+    lib.idx_version.argtypes = []
+    lib.idx_workspace_bytes.restype = ctypes.c_size_t
+    lib.idx_workspace_bytes.argtypes = [ctypes.c_int, _I32, _I64, _I32]
+    _lib = lib
+    return lib
+
+
+def _hip_rt():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_P), ctypes.c_uint]
+        _hip.hipEventCreateWithFlags.restype = ctypes.c_int
+        _hip.hipEventDestroy.argtypes = [_P]
+        _hip.hipEventDestroy.restype = ctypes.c_int
+        _hip.hipStreamWaitEvent.argtypes = [_P, _P, ctypes.c_uint]
+        _hip.hipStreamWaitEvent.restype = ctypes.c_int
+    return _hip
+
+
+def stream_wait_table(tbl: "Table", stream=None):
+    """Make `stream` (default: current) wait until tbl.ready has been reached."""
+    if tbl.ready is None:
+        return
+    rc = _hip_rt().hipStreamWaitEvent(_stream(stream), tbl.ready, 0)
+    if rc != 0:
+        raise IdxError(f"hipStreamWaitEvent failed ({rc})")
+
+
+def _check(status: int, name: str):
+    if status != 0:
+        msg = load().idx_last_error().decode(errors="replace")
+        raise IdxError(f"{name} failed ({status}): {msg}")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _req(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise IdxError(f"{name}: expected a tensor")
+    if t.dtype != dtype:
+        raise IdxError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise IdxError(f"{name}: must be contiguous")
+    if not t.is_cuda:
+        raise IdxError(f"{name}: must be on the GPU")
+    return t
+
+
+# ---------------------------------------------------------------------------
+# operand bundles
+# ---------------------------------------------------------------------------
+
+class Query:
+    """One index layer's query batch: vals u8 [R,H,64], scales u8 [R,H,4], w f32 [R,H]."""
+
+    def __init__(self, vals, scales, w):
+        self.vals = _req(vals, torch.uint8, "vals")
+        self.scales = _req(scales, torch.uint8, "scales")
+        self.w = _req(w, torch.float32, "w")
+        self.rows, self.heads = int(vals.shape[0]), int(vals.shape[1])
+        if tuple(vals.shape) != (self.rows, self.heads, 64) or \
+           tuple(scales.shape) != (self.rows, self.heads, 4) or tuple(w.shape) != (self.rows, self.heads):
+            raise IdxError("query shapes must be [R,H,64], [R,H,4], [R,H]")
+
+    def c(self):
+        return _Query(_ptr(self.vals), _ptr(self.scales), _ptr(self.w), self.rows, self.heads, 128)
+
+
+class KPool:
+    """Paged MXFP4 index-K pool u8 [pages, 64*68] and page table i32 [num_req, max_pages]."""
+
+    def __init__(self, pool, page_table, page_size: int = 64):
+        self.pool = _req(pool, torch.uint8, "pool")
+        self.page_table = _req(page_table, torch.int32, "page_table")
+        self.page_size = page_size
+        if pool.dim() != 2 or pool.shape[1] != page_size * 68:
+            raise IdxError("pool must be [num_pages, page_size * 68]")
+
+    def c(self):
+        return _KPool(_ptr(self.pool), int(self.pool.shape[0]), self.page_size, 128,
+                      _ptr(self.page_table), int(self.page_table.shape[0]),
+                      int(self.page_table.shape[1]))
+
+
+class Rows:
+    """Per-row request ids, compress_lens and optional output offsets (all i32 [R])."""
+
+    def __init__(self, req, lens, pos_offset=None):
+        self.req = _req(req, torch.int32, "req")
+        self.len = _req(lens, torch.int32, "len")
+        self.pos_offset = None if pos_offset is None else _req(pos_offset, torch.int32, "pos_offset")
+        self.rows = int(req.shape[0])
+
+    def c(self):
+        return _Rows(_ptr(self.req), _ptr(self.len), _ptr(self.pos_offset), self.rows)
+
+
+class Table:
+    """A published candidate table; allocated on the current (consumer) stream."""
+
+    def __init__(self, rows: int, kb: int, device="cuda", with_event: bool = True):
+        lib = load()
+        i32 = dict(dtype=torch.int32, device=device)
+        self.rows, self.kb = rows, kb
+        self.blocks = torch.empty((rows, kb), **i32)
+        self.n_kept = torch.empty((rows,), **i32)
+        self.phys = torch.empty((rows, kb), **i32)
+        self.valid_len = torch.empty((rows,), **i32)
+        self.len = torch.empty((rows,), **i32)
+        self.req = torch.empty((rows,), **i32)
+        nb = lib.idx_workspace_bytes(OP_SCHEDULE, rows, kb, 0)
+        self.schedule = torch.empty((max(nb, 16),), dtype=torch.uint8, device=device)
+        self.ready = None
+        if with_event:
+            ev = _P()
+            rc = _hip_rt().hipEventCreateWithFlags(ctypes.byref(ev), 0x2)  # disable timing
+            if rc != 0:
+                raise IdxError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ready = ev
+
+    def tensors(self):
+        return [self.blocks, self.n_kept, self.phys, self.valid_len, self.len, self.req, self.schedule]
+
+    def record_stream(self, stream):
+        for t in self.tensors():
+            t.record_stream(stream)
+
+    def c(self):
+        return _Table(_ptr(self.blocks), _ptr(self.n_kept), _ptr(self.phys), _ptr(self.valid_len),
+                      _ptr(self.len), _ptr(self.req), _ptr(self.schedule),
+                      int(self.schedule.numel()), self.rows, self.kb, self.ready)
+
+    def __del__(self):
+        if getattr(self, "ready", None) is not None and _hip is not None:
+            try:
+                _hip.hipEventDestroy(self.ready)
+            except Exception:
+                pass
+            self.ready = None
+
+
+# ---------------------------------------------------------------------------
+# the seven calls
+# ---------------------------------------------------------------------------
+
+def idx_workspace_bytes(op: int, rows: int, width: int, k: int) -> int:
+    return int(load().idx_workspace_bytes(op, rows, width, k))
+
+
+def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, stream=None):
+    _req(S, torch.float32, "S")
+    q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
+    _check(load().idx_score_dense(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
+                                  _ptr(S), S.stride(0), _stream(stream)), "idx_score_dense")
+
+
+def idx_amax8_varlen(S, lens, keys, skip_le_blocks: int = 0, stream=None):
+    _req(S, torch.float32, "S"); _req(lens, torch.int32, "len"); _req(keys, torch.float32, "keys")
+    _check(load().idx_amax8_varlen(_ptr(S), S.stride(0), _ptr(lens), int(lens.shape[0]), _ptr(keys),
+                                   keys.stride(0), int(skip_le_blocks), _stream(stream)),
+           "idx_amax8_varlen")
+
+
+def idx_topk_blocks(keys, lens, kb: int, blocks, n_kept, stream=None):
+    _req(keys, torch.float32, "keys"); _req(lens, torch.int32, "len")
+    _req(blocks, torch.int32, "blocks"); _req(n_kept, torch.int32, "n_kept")
+    if blocks.shape[-1] != kb:
+        raise IdxError("blocks must be [rows, kb]")
+    _check(load().idx_topk_blocks(_ptr(keys), keys.stride(0), _ptr(lens), int(lens.shape[0]), kb,
+                                  _ptr(blocks), _ptr(n_kept), None, 0, _stream(stream)),
+           "idx_topk_blocks")
+
+
+def idx_expand_candidates(kp: KPool, rows: Rows, tbl: Table, stream=None):
+    kp_c, rows_c, t_c = kp.c(), rows.c(), tbl.c()
+    _check(load().idx_expand_candidates(ctypes.byref(kp_c), ctypes.byref(rows_c), ctypes.byref(t_c),
+                                        _stream(stream)), "idx_expand_candidates")
+
+
+def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, stream=None):
+    _req(T, torch.float32, "T")
+    q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
+    _check(load().idx_score_sparse_paged(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
+                                         _ptr(T), T.stride(0), _stream(stream)),
+           "idx_score_sparse_paged")
+
+
+def idx_topk_rows(X, valid, k: int, out, mode: int = COLS_IDENTITY, blocks=None, pos_offset=None,
+                  stream=None):
+    _req(X, torch.float32, "X"); _req(valid, torch.int32, "valid"); _req(out, torch.int32, "out")
+    if out.shape[-1] != k:
+        raise IdxError("out must be [rows, k]")
+    kb = 0
+    if blocks is not None:
+        _req(blocks, torch.int32, "blocks")
+        kb = int(blocks.shape[-1])
+    if pos_offset is not None:
+        _req(pos_offset, torch.int32, "pos_offset")
+    _check(load().idx_topk_rows(_ptr(X), X.stride(0), _ptr(valid), int(valid.shape[0]), k, mode,
+                                _ptr(blocks), kb, _ptr(pos_offset), _ptr(out), None, 0,
+                                _stream(stream)), "idx_topk_rows")
+
+
+def idx_prefill_tail(full: Table, rows_per_req, tail_len, tail: Table, ws=None, stream=None):
+    import numpy as np
+    rpr = np.ascontiguousarray(np.asarray(rows_per_req, dtype=np.int32))
+    tl = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int32))
+    if ws is None:
+        n = max(1, idx_workspace_bytes(OP_TAIL, tail.rows, 0, 0))
+        ws = torch.empty((n,), dtype=torch.uint8, device=tail.blocks.device)
+        if stream is not None:
+            ws.record_stream(stream)
+    f_c, t_c = full.c(), tail.c()
+    _check(load().idx_prefill_tail(ctypes.byref(f_c), rpr.ctypes.data_as(_P), tl.ctypes.data_as(_P),
+                                   len(rpr), ctypes.byref(t_c), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "idx_prefill_tail")
+    return ws

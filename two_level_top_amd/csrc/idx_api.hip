@@ -1,0 +1,274 @@
+// C ABI entry points (include/idx.h): host-side validation, then launches on
+// the caller's stream.  Nothing is enqueued when validation fails.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "idx.h"
+#include "idx_internal.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+idx_status fail(idx_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+idx_status ok() {
+  g_err[0] = '\0';
+  return IDX_OK;
+}
+
+idx_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(IDX_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+idx_status check_query(const idx_query* q, const char* fn) {
+  if (!q) return fail(IDX_E_ARG, "%s: query is NULL", fn);
+  if (q->rows < 0) return fail(IDX_E_ARG, "%s: query rows < 0", fn);
+  if (q->dim != idxk::kDim) return fail(IDX_E_UNSUPPORTED, "%s: dim %d (only 128)", fn, q->dim);
+  if (q->heads < 1 || q->heads > 64)
+    return fail(IDX_E_UNSUPPORTED, "%s: heads %d (1..64)", fn, q->heads);
+  if (q->rows > 0 && (!q->vals || !q->scales || !q->w))
+    return fail(IDX_E_ARG, "%s: query vals/scales/w is NULL", fn);
+  if (!aligned(q->vals, 16)) return fail(IDX_E_ALIGN, "%s: query vals must be 16-byte aligned", fn);
+  if (!aligned(q->w, 4)) return fail(IDX_E_ALIGN, "%s: query w must be 4-byte aligned", fn);
+  return IDX_OK;
+}
+
+idx_status check_pool(const idx_kpool* kp, const char* fn, bool need_table) {
+  if (!kp) return fail(IDX_E_ARG, "%s: kpool is NULL", fn);
+  if (kp->page_size != idxk::kPage)
+    return fail(IDX_E_UNSUPPORTED, "%s: page_size %d (only 64)", fn, kp->page_size);
+  if (kp->dim != idxk::kDim) return fail(IDX_E_UNSUPPORTED, "%s: pool dim %d (only 128)", fn, kp->dim);
+  if (kp->num_pages < 1 || !kp->pool) return fail(IDX_E_ARG, "%s: empty or NULL pool", fn);
+  if (!aligned(kp->pool, 16)) return fail(IDX_E_ALIGN, "%s: pool must be 16-byte aligned", fn);
+  if (need_table) {
+    if (!kp->page_table) return fail(IDX_E_ARG, "%s: page_table is NULL", fn);
+    if (kp->num_req < 1 || kp->max_pages < 1)
+      return fail(IDX_E_ARG, "%s: num_req and max_pages must be >= 1", fn);
+  }
+  return IDX_OK;
+}
+
+idx_status check_rows(const idx_rows* r, const char* fn) {
+  if (!r) return fail(IDX_E_ARG, "%s: rows is NULL", fn);
+  if (r->rows < 0) return fail(IDX_E_ARG, "%s: rows < 0", fn);
+  if (r->rows > 0 && (!r->req || !r->len)) return fail(IDX_E_ARG, "%s: req/len is NULL", fn);
+  return IDX_OK;
+}
+
+idx_status check_table(const idx_table* t, const char* fn, bool need_schedule) {
+  if (!t) return fail(IDX_E_ARG, "%s: table is NULL", fn);
+  if (t->rows < 0) return fail(IDX_E_ARG, "%s: table rows < 0", fn);
+  if (t->kb < 1) return fail(IDX_E_ARG, "%s: table kb < 1", fn);
+  if (t->rows > 0 && (!t->blocks || !t->n_kept || !t->phys || !t->valid_len || !t->len || !t->req))
+    return fail(IDX_E_ARG, "%s: a table buffer is NULL", fn);
+  if (need_schedule) {
+    if (!t->schedule) return fail(IDX_E_WORKSPACE, "%s: table schedule is NULL", fn);
+    const size_t need = idxk::schedule_bytes(t->rows, t->kb);
+    if (t->schedule_bytes < need)
+      return fail(IDX_E_WORKSPACE, "%s: schedule_bytes %zu < %zu", fn, t->schedule_bytes, need);
+    if (!aligned(t->schedule, 4)) return fail(IDX_E_ALIGN, "%s: schedule must be 4-byte aligned", fn);
+  }
+  return IDX_OK;
+}
+
+#define TRY(x)                       \
+  do {                               \
+    idx_status s_ = (x);             \
+    if (s_ != IDX_OK) return s_;     \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* idx_last_error(void) { return g_err; }
+
+const char* idx_version(void) { return "idx 0.1 gfx950"; }
+
+size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k) {
+  (void)width;
+  (void)k;
+  switch (op) {
+    case IDX_OP_TOPK_BLOCKS:
+    case IDX_OP_TOPK_ROWS:
+      return 0;
+    case IDX_OP_SCHEDULE:
+      return idxk::schedule_bytes(rows, (int)width);
+    case IDX_OP_TAIL:
+      return (size_t)(rows > 0 ? rows : 0) * sizeof(int32_t);
+    default:
+      return 0;
+  }
+}
+
+idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows, float* S,
+                           int64_t ld, hipStream_t stream) {
+  const char* fn = "idx_score_dense";
+  TRY(check_query(q, fn));
+  TRY(check_pool(kp, fn, true));
+  TRY(check_rows(rows, fn));
+  if (q->rows != rows->rows) return fail(IDX_E_SHAPE, "%s: query rows %d != rows %d", fn, q->rows, rows->rows);
+  if (ld < 1) return fail(IDX_E_ARG, "%s: ld < 1", fn);
+  if (rows->rows == 0) return ok();
+  if (!S) return fail(IDX_E_ARG, "%s: S is NULL", fn);
+  if (!aligned(S, 4)) return fail(IDX_E_ALIGN, "%s: S must be 4-byte aligned", fn);
+  idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
+  idxk::PoolArgs pa{kp->pool, kp->num_pages, kp->page_table, kp->num_req, kp->max_pages};
+  return hip_status(idxk::launch_score_dense(qa, pa, rows->req, rows->len, S, ld, stream), fn);
+}
+
+idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int32_t rows,
+                            float* keys, int64_t ldk, int32_t skip_le_blocks, hipStream_t stream) {
+  const char* fn = "idx_amax8_varlen";
+  if (rows < 0) return fail(IDX_E_ARG, "%s: rows < 0", fn);
+  if (skip_le_blocks < 0) return fail(IDX_E_ARG, "%s: skip_le_blocks < 0", fn);
+  if (ld < idxk::kBlock || ld % idxk::kBlock != 0)
+    return fail(IDX_E_ALIGN, "%s: ld %lld must be a positive multiple of 8 (32-byte blocks)", fn, (long long)ld);
+  if (ldk < 1) return fail(IDX_E_ARG, "%s: ldk must hold at least one key per row", fn);
+  if (rows == 0) return ok();
+  if (!S || !len || !keys) return fail(IDX_E_ARG, "%s: S/len/keys is NULL", fn);
+  if (!aligned(S, 32)) return fail(IDX_E_ALIGN, "%s: S must be 32-byte aligned", fn);
+  if (!aligned(keys, 4)) return fail(IDX_E_ALIGN, "%s: keys must be 4-byte aligned", fn);
+  return hip_status(idxk::launch_amax8(S, ld, len, rows, keys, ldk, skip_le_blocks, stream), fn);
+}
+
+idx_status idx_topk_blocks(const float* keys, int64_t ldk, const int32_t* len, int32_t rows,
+                           int32_t kb, int32_t* blocks, int32_t* n_kept, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "idx_topk_blocks";
+  (void)ws;
+  (void)ws_bytes;
+  if (rows < 0) return fail(IDX_E_ARG, "%s: rows < 0", fn);
+  if (kb < 1) return fail(IDX_E_ARG, "%s: kb < 1", fn);
+  if (ldk < 1) return fail(IDX_E_ARG, "%s: ldk < 1", fn);
+  if (rows == 0) return ok();
+  if (!keys || !len || !blocks || !n_kept) return fail(IDX_E_ARG, "%s: a pointer is NULL", fn);
+  return hip_status(idxk::launch_topk(3, keys, ldk, nullptr, len, rows, kb, ldk, nullptr, kb,
+                                      nullptr, blocks, n_kept, stream), fn);
+}
+
+idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_table* tbl,
+                                 hipStream_t stream) {
+  const char* fn = "idx_expand_candidates";
+  TRY(check_pool(kp, fn, true));
+  TRY(check_rows(rows, fn));
+  TRY(check_table(tbl, fn, true));
+  if (tbl->rows != rows->rows)
+    return fail(IDX_E_SHAPE, "%s: table rows %d != rows %d", fn, tbl->rows, rows->rows);
+  idxk::PoolArgs pa{kp->pool, kp->num_pages, kp->page_table, kp->num_req, kp->max_pages};
+  hipError_t e = idxk::launch_expand(pa, rows->req, rows->len, rows->rows, tbl->kb, tbl->blocks,
+                                     tbl->n_kept, tbl->phys, tbl->valid_len, tbl->len, tbl->req,
+                                     tbl->schedule, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (tbl->ready) return hip_status(hipEventRecord(tbl->ready, stream), "idx_expand_candidates: hipEventRecord");
+  return ok();
+}
+
+idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
+                                  float* T, int64_t ld, hipStream_t stream) {
+  const char* fn = "idx_score_sparse_paged";
+  TRY(check_query(q, fn));
+  TRY(check_pool(kp, fn, false));
+  TRY(check_table(tbl, fn, true));
+  if (q->rows != tbl->rows) return fail(IDX_E_SHAPE, "%s: query rows %d != table rows %d", fn, q->rows, tbl->rows);
+  if (ld < (int64_t)tbl->kb * idxk::kBlock)
+    return fail(IDX_E_SHAPE, "%s: ld %lld < kb * 8 = %lld", fn, (long long)ld, (long long)tbl->kb * 8);
+  if (tbl->rows > 0 && !T) return fail(IDX_E_ARG, "%s: T is NULL", fn);
+  if (!aligned(T, 4)) return fail(IDX_E_ALIGN, "%s: T must be 4-byte aligned", fn);
+  if (tbl->ready) {
+    hipError_t e = hipStreamWaitEvent(stream, tbl->ready, 0);
+    if (e != hipSuccess) return hip_status(e, "idx_score_sparse_paged: hipStreamWaitEvent");
+  }
+  if (tbl->rows == 0) return ok();
+  idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
+  return hip_status(idxk::launch_score_sparse(qa, kp->pool, kp->num_pages, tbl->phys, tbl->n_kept,
+                                              tbl->valid_len, tbl->rows, tbl->kb, tbl->schedule, T,
+                                              ld, stream), fn);
+}
+
+idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32_t rows, int32_t k,
+                         int mode, const int32_t* blocks, int32_t kb, const int32_t* pos_offset,
+                         int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "idx_topk_rows";
+  (void)ws;
+  (void)ws_bytes;
+  if (rows < 0) return fail(IDX_E_ARG, "%s: rows < 0", fn);
+  if (k < 1) return fail(IDX_E_ARG, "%s: k < 1", fn);
+  if (ld < 1) return fail(IDX_E_ARG, "%s: ld < 1", fn);
+  if (mode != IDX_COLS_IDENTITY && mode != IDX_COLS_BLOCKMAP && mode != IDX_COLS_GATHER)
+    return fail(IDX_E_ARG, "%s: unknown column mode %d", fn, mode);
+  if (mode != IDX_COLS_IDENTITY) {
+    if (!blocks && rows > 0) return fail(IDX_E_ARG, "%s: blocks is NULL for a block-mapped mode", fn);
+    if (kb < 1) return fail(IDX_E_ARG, "%s: kb < 1 for a block-mapped mode", fn);
+    if (mode == IDX_COLS_BLOCKMAP && ld < (int64_t)kb * idxk::kBlock)
+      return fail(IDX_E_SHAPE, "%s: ld %lld < kb * 8 in block-map mode", fn, (long long)ld);
+  }
+  if (rows == 0) return ok();
+  if (!X || !valid || !out) return fail(IDX_E_ARG, "%s: X/valid/out is NULL", fn);
+  return hip_status(idxk::launch_topk(mode, X, ld, valid, nullptr, rows, k, ld, blocks, kb,
+                                      pos_offset, out, nullptr, stream), fn);
+}
+
+idx_status idx_prefill_tail(const idx_table* full, const int32_t* rows_per_req_host,
+                            const int32_t* tail_len_host, int32_t num_req, idx_table* tail,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "idx_prefill_tail";
+  TRY(check_table(full, fn, false));
+  TRY(check_table(tail, fn, true));
+  if (num_req < 0) return fail(IDX_E_ARG, "%s: num_req < 0", fn);
+  if (num_req > 0 && (!rows_per_req_host || !tail_len_host))
+    return fail(IDX_E_ARG, "%s: rows_per_req_host/tail_len_host is NULL", fn);
+  if (full->kb != tail->kb) return fail(IDX_E_SHAPE, "%s: kb %d != %d", fn, full->kb, tail->kb);
+  std::vector<int32_t> src;
+  int64_t start = 0;
+  for (int j = 0; j < num_req; ++j) {
+    const int32_t n = rows_per_req_host[j], t = tail_len_host[j];
+    if (n < 0 || t < 0 || t > n)
+      return fail(IDX_E_ARG, "%s: request %d has rows %d, tail %d", fn, j, n, t);
+    for (int32_t i = n - t; i < n; ++i) src.push_back((int32_t)(start + i));
+    start += n;
+  }
+  if (start != full->rows)
+    return fail(IDX_E_SHAPE, "%s: rows_per_req sums to %lld, table has %d rows", fn, (long long)start, full->rows);
+  if ((int64_t)src.size() != tail->rows)
+    return fail(IDX_E_SHAPE, "%s: tail lengths sum to %zu, tail table has %d rows", fn, src.size(), tail->rows);
+  const size_t need = src.size() * sizeof(int32_t);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(IDX_E_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
+  hipError_t e = hipSuccess;
+  if (full->ready) {
+    e = hipStreamWaitEvent(stream, full->ready, 0);
+    if (e != hipSuccess) return hip_status(e, "idx_prefill_tail: hipStreamWaitEvent");
+  }
+  if (need > 0) {
+    e = hipMemcpyAsync(ws, src.data(), need, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_status(e, "idx_prefill_tail: hipMemcpyAsync");
+    // the host vector dies with this call: make sure the copy has read it
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e, "idx_prefill_tail: hipStreamSynchronize");
+  }
+  e = idxk::launch_tail_gather(static_cast<const int32_t*>(ws), tail->rows, tail->kb, full->blocks,
+                               full->n_kept, full->phys, full->valid_len, full->len, full->req,
+                               tail->blocks, tail->n_kept, tail->phys, tail->valid_len, tail->len,
+                               tail->req, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  e = idxk::launch_schedule(tail->n_kept, tail->rows, tail->kb, tail->schedule, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (tail->ready) return hip_status(hipEventRecord(tail->ready, stream), "idx_prefill_tail: hipEventRecord");
+  return ok();
+}
+
+}  // extern "C"

@@ -290,3 +290,33 @@ def custom(name: str, cfg: int, heads: int, kb: int, kc: int, ctx, rows_per_req,
 
 
 CONFIGS = {"tiny": tiny, "decode": decode, "prefill": prefill, "long": long_chunk, "mixed": mixed}
+
+
+# ---------------------------------------------------------------------------
+# synthetic score / key matrices for the selection steps alone
+# ---------------------------------------------------------------------------
+
+def random_matrix(seed: int, rows: int, width: int, ties: bool = True,
+                  specials: bool = True) -> np.ndarray:
+    """float32 [rows, width] ~ N(0, 8^2) with, optionally, exact ties (values
+    snapped to a coarse grid on a third of the rows) and +-0 / +-inf entries."""
+    r = _rng(900, seed)
+    x = (r.standard_normal((rows, width), dtype=np.float32) * np.float32(8.0)).astype(np.float32)
+    if ties and rows:
+        sel = r.random(rows) < 0.34
+        x[sel] = np.round(x[sel] * 2.0) / 2.0
+    if specials and rows and width:
+        n = max(1, rows * width // 500)
+        ri, ci = r.integers(0, rows, n), r.integers(0, width, n)
+        vals = np.array([0.0, -0.0, np.inf, -np.inf], np.float32)
+        x[ri, ci] = vals[r.integers(0, 4, n)]
+    return x
+
+
+def random_lengths(seed: int, rows: int, lo: int, hi: int, extra=()) -> np.ndarray:
+    """int32 [rows] uniform in [lo, hi], the given values placed first."""
+    r = _rng(901, seed)
+    out = r.integers(lo, hi, size=rows, endpoint=True).astype(np.int32)
+    for i, v in enumerate(extra[:rows]):
+        out[i] = v
+    return out
