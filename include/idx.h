@@ -155,7 +155,8 @@ enum {
   IDX_OP_TOPK_BLOCKS = 1, /* idx_topk_blocks: rows, width = ldk, k = kb     */
   IDX_OP_TOPK_ROWS = 2,   /* idx_topk_rows:   rows, width = columns, k      */
   IDX_OP_SCHEDULE = 3,    /* idx_table.schedule: rows, width = kb           */
-  IDX_OP_TAIL = 4         /* idx_prefill_tail: rows = tail rows             */
+  IDX_OP_TAIL = 4,        /* idx_prefill_tail: rows = tail rows             */
+  IDX_OP_SCORE = 5        /* idx_score_dense / idx_score_sparse_paged: rows */
 };
 size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k);
 
@@ -167,9 +168,13 @@ size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k);
  *   S[r * ld + p] = score(r, p) for p < len[r]; S beyond len[r] is not written.
  * q->rows == rows->rows; ld >= max len (not checked: device data) and ld >= 1;
  * S must be 4-byte aligned.
+ * ws: idx_workspace_bytes(IDX_OP_SCORE, q->rows, 0, 0) device bytes, 16-byte
+ * aligned; the call first writes there each row's weight-folded query
+ * sum_h (w_h/2) q_h as 16 MXFP4 terms (exact), which lets the kernel use
+ * relu(s) = (s + |s|)/2 with the linear half on the MFMA.
  */
 idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows,
-                           float* S, int64_t ld, hipStream_t stream);
+                           float* S, int64_t ld, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * idx_amax8_varlen -- block keys (the block_amax.cuh contract quoted in the
@@ -218,9 +223,11 @@ idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_
  *   T[r * ld + c] = score'(r, blocks[r][c/8]*8 + c%8) for c < valid_len[r];
  *   T beyond valid_len[r] is not written.
  * q->rows == tbl->rows; ld >= tbl->kb * 8.
+ * ws: as for idx_score_dense (IDX_OP_SCORE, q->rows).
  */
 idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
-                                  float* T, int64_t ld, hipStream_t stream);
+                                  float* T, int64_t ld, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* Column modes of idx_topk_rows. */
 enum {

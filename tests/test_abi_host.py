@@ -87,19 +87,23 @@ def test_score_validation(lib):
     t, q, kp, rows, tbl = _structs()
     P = ctypes.byref
     bad = t._Query(FAKE, FAKE, FAKE, 4, 64, 64)
-    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, None) == -4        # dim
+    W = 1 << 20
+    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, FAKE, W, None) == -4   # dim
     bad = t._Query(FAKE, FAKE, FAKE, 4, 65, 128)
-    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, None) == -4        # heads
+    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, FAKE, W, None) == -4   # heads
     bad = t._Query(FAKE_ODD, FAKE, FAKE, 4, 64, 128)
-    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, None) == -2        # alignment
+    assert lib.idx_score_dense(P(bad), P(kp), P(rows), FAKE, 1024, FAKE, W, None) == -2   # alignment
     badkp = t._KPool(FAKE, 16, 32, 128, FAKE, 1, 16)
-    assert lib.idx_score_dense(P(q), P(badkp), P(rows), FAKE, 1024, None) == -4       # page size
+    assert lib.idx_score_dense(P(q), P(badkp), P(rows), FAKE, 1024, FAKE, W, None) == -4  # page size
     r3 = t._Rows(FAKE, FAKE, None, 3)
-    assert lib.idx_score_dense(P(q), P(kp), P(r3), FAKE, 1024, None) == -3            # rows mismatch
-    assert lib.idx_score_dense(None, P(kp), P(rows), FAKE, 1024, None) == -1
+    assert lib.idx_score_dense(P(q), P(kp), P(r3), FAKE, 1024, FAKE, W, None) == -3       # rows
+    assert lib.idx_score_dense(None, P(kp), P(rows), FAKE, 1024, FAKE, W, None) == -1
+    assert lib.idx_score_dense(P(q), P(kp), P(rows), FAKE, 1024, FAKE, 100, None) == -6   # workspace
+    assert lib.idx_score_dense(P(q), P(kp), P(rows), FAKE, 1024, FAKE_ODD, W, None) == -2
     small = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 16, None)
-    assert lib.idx_score_sparse_paged(P(q), P(kp), P(small), FAKE, 128, None) == -6   # schedule size
-    assert lib.idx_score_sparse_paged(P(q), P(kp), P(tbl), FAKE, 64, None) == -3      # ld < kb*8
+    assert lib.idx_score_sparse_paged(P(q), P(kp), P(small), FAKE, 128, FAKE, W, None) == -6  # schedule
+    assert lib.idx_score_sparse_paged(P(q), P(kp), P(tbl), FAKE, 64, FAKE, W, None) == -3     # ld
+    assert lib.idx_score_sparse_paged(P(q), P(kp), P(tbl), FAKE, 128, None, 0, None) == -6   # workspace
     assert lib.idx_expand_candidates(P(kp), P(r3), P(tbl), None) == -3
 
 
@@ -122,3 +126,4 @@ def test_workspace_sizes(lib):
     assert lib.idx_workspace_bytes(3, 16384, 2048, 0) == 16 + 16384 * 32 * 8
     assert lib.idx_workspace_bytes(4, 100, 0, 0) == 400
     assert lib.idx_workspace_bytes(1, 100, 32768, 2048) == 0
+    assert lib.idx_workspace_bytes(5, 100, 0, 0) == 100 * 1088

@@ -21,14 +21,14 @@ __all__ = [
     "IdxError", "Query", "KPool", "Rows", "Table", "load",
     "idx_score_dense", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
     "idx_score_sparse_paged", "idx_topk_rows", "idx_prefill_tail", "idx_workspace_bytes",
-    "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table",
+    "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table", "score_workspace",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libidx.so")
 
 COLS_IDENTITY, COLS_BLOCKMAP, COLS_GATHER = 0, 1, 2
-OP_TOPK_BLOCKS, OP_TOPK_ROWS, OP_SCHEDULE, OP_TAIL = 1, 2, 3, 4
+OP_TOPK_BLOCKS, OP_TOPK_ROWS, OP_SCHEDULE, OP_TAIL, OP_SCORE = 1, 2, 3, 4, 5
 INT32_MAX = 2 ** 31 - 1
 
 
@@ -75,11 +75,11 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     st = ctypes.c_int
     sig = {
-        "idx_score_dense": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P],
+        "idx_score_dense": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_amax8_varlen": [_P, _I64, _P, _I32, _P, _I64, _I32, _P],
         "idx_topk_blocks": [_P, _I64, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
         "idx_expand_candidates": [ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), ctypes.POINTER(_Table), _P],
-        "idx_score_sparse_paged": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P],
+        "idx_score_sparse_paged": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_topk_rows": [_P, _I64, _P, _I32, _I32, ctypes.c_int, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
         "idx_prefill_tail": [ctypes.POINTER(_Table), _P, _P, _I32, ctypes.POINTER(_Table), _P, ctypes.c_size_t, _P],
     }
@@ -250,11 +250,27 @@ def idx_workspace_bytes(op: int, rows: int, width: int, k: int) -> int:
     return int(load().idx_workspace_bytes(op, rows, width, k))
 
 
-def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, stream=None):
+def score_workspace(rows: int, device="cuda") -> torch.Tensor:
+    """Workspace of idx_score_dense / idx_score_sparse_paged for `rows` query rows."""
+    n = max(16, idx_workspace_bytes(OP_SCORE, rows, 0, 0))
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def _score_ws(ws, rows, device, stream):
+    if ws is None:
+        ws = score_workspace(rows, device)
+        if stream is not None:
+            ws.record_stream(stream)
+    return _req(ws, torch.uint8, "ws")
+
+
+def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, ws=None, stream=None):
     _req(S, torch.float32, "S")
+    ws = _score_ws(ws, q.rows, S.device, stream)
     q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
     _check(load().idx_score_dense(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
-                                  _ptr(S), S.stride(0), _stream(stream)), "idx_score_dense")
+                                  _ptr(S), S.stride(0), _ptr(ws), ws.numel(), _stream(stream)),
+           "idx_score_dense")
 
 
 def idx_amax8_varlen(S, lens, keys, skip_le_blocks: int = 0, stream=None):
@@ -280,11 +296,13 @@ def idx_expand_candidates(kp: KPool, rows: Rows, tbl: Table, stream=None):
                                         _stream(stream)), "idx_expand_candidates")
 
 
-def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, stream=None):
+def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=None, stream=None):
     _req(T, torch.float32, "T")
+    ws = _score_ws(ws, q.rows, T.device, stream)
     q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
     _check(load().idx_score_sparse_paged(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
-                                         _ptr(T), T.stride(0), _stream(stream)),
+                                         _ptr(T), T.stride(0), _ptr(ws), ws.numel(),
+                                         _stream(stream)),
            "idx_score_sparse_paged")
 
 

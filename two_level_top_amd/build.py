@@ -15,8 +15,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # gfx950 only.  Packed fp32 ops are switched off: the compiler must not form
 # v_pk_{add,mul,fma}_f32 from scalar code.
+# MFMA results stay in VGPRs (no accumulator-register round trips).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

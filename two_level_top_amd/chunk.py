@@ -28,7 +28,7 @@ import torch
 
 from . import (COLS_BLOCKMAP, COLS_GATHER, COLS_IDENTITY, KPool, Query, Rows, Table,
                idx_amax8_varlen, idx_expand_candidates, idx_score_dense, idx_score_sparse_paged,
-               idx_topk_blocks, idx_topk_rows, stream_wait_table)
+               idx_topk_blocks, idx_topk_rows, score_workspace, stream_wait_table)
 
 
 def _dev(a, dtype, device):
@@ -61,6 +61,7 @@ class Chunk:
         self.src_top = torch.empty((self.R, self.k_src), dtype=torch.int32, device=device)
         self.cons_top = [torch.empty((self.R, self.kc), dtype=torch.int32, device=device)
                          for _ in range(ncons)]
+        self.ws = score_workspace(self.R, device)      # folded queries of the layer being scored
         self.side = torch.cuda.Stream(device=device)
         self.scores_ready = torch.cuda.Event()
         self.recorder = None     # optional: object with mark(name) (timing only)
@@ -72,7 +73,7 @@ class Chunk:
     # -- the source layer ---------------------------------------------------
     def score_source(self, stream=None):
         self._mark("dense<")
-        idx_score_dense(self.queries[0], self.kp, self.rows, self.S, stream=stream)
+        idx_score_dense(self.queries[0], self.kp, self.rows, self.S, ws=self.ws, stream=stream)
         self._mark("dense>")
 
     def publish(self):
@@ -108,7 +109,7 @@ class Chunk:
     def consumer(self, i: int):
         T = self.T[i % len(self.T)]
         self._mark(f"sparse{i}<")
-        idx_score_sparse_paged(self.queries[1 + i], self.kp, self.table, T)
+        idx_score_sparse_paged(self.queries[1 + i], self.kp, self.table, T, ws=self.ws)
         self._mark(f"sparse{i}>")
         idx_topk_rows(T, self.table.valid_len, self.kc, self.cons_top[i], mode=COLS_BLOCKMAP,
                       blocks=self.table.blocks, pos_offset=self.rows.pos_offset)

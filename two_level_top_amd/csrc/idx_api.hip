@@ -68,6 +68,15 @@ idx_status check_rows(const idx_rows* r, const char* fn) {
   return IDX_OK;
 }
 
+idx_status check_score_ws(const void* ws, size_t ws_bytes, int rows, const char* fn) {
+  const size_t need = (size_t)(rows > 0 ? rows : 0) * idxk::kFoldRowBytes;
+  if (need == 0) return IDX_OK;
+  if (!ws || ws_bytes < need)
+    return fail(IDX_E_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws ? ws_bytes : (size_t)0, need);
+  if (!aligned(ws, 16)) return fail(IDX_E_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return IDX_OK;
+}
+
 idx_status check_table(const idx_table* t, const char* fn, bool need_schedule) {
   if (!t) return fail(IDX_E_ARG, "%s: table is NULL", fn);
   if (t->rows < 0) return fail(IDX_E_ARG, "%s: table rows < 0", fn);
@@ -109,13 +118,15 @@ size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k) {
       return idxk::schedule_bytes(rows, (int)width);
     case IDX_OP_TAIL:
       return (size_t)(rows > 0 ? rows : 0) * sizeof(int32_t);
+    case IDX_OP_SCORE:
+      return (size_t)(rows > 0 ? rows : 0) * idxk::kFoldRowBytes;
     default:
       return 0;
   }
 }
 
 idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows, float* S,
-                           int64_t ld, hipStream_t stream) {
+                           int64_t ld, void* ws, size_t ws_bytes, hipStream_t stream) {
   const char* fn = "idx_score_dense";
   TRY(check_query(q, fn));
   TRY(check_pool(kp, fn, true));
@@ -125,9 +136,13 @@ idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_ro
   if (rows->rows == 0) return ok();
   if (!S) return fail(IDX_E_ARG, "%s: S is NULL", fn);
   if (!aligned(S, 4)) return fail(IDX_E_ALIGN, "%s: S must be 4-byte aligned", fn);
+  TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
   idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
   idxk::PoolArgs pa{kp->pool, kp->num_pages, kp->page_table, kp->num_req, kp->max_pages};
-  return hip_status(idxk::launch_score_dense(qa, pa, rows->req, rows->len, S, ld, stream), fn);
+  uint8_t* fold = static_cast<uint8_t*>(ws);
+  hipError_t e = idxk::launch_fold_query(qa, fold, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(idxk::launch_score_dense(qa, fold, pa, rows->req, rows->len, S, ld, stream), fn);
 }
 
 idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int32_t rows,
@@ -178,7 +193,8 @@ idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_
 }
 
 idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
-                                  float* T, int64_t ld, hipStream_t stream) {
+                                  float* T, int64_t ld, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   const char* fn = "idx_score_sparse_paged";
   TRY(check_query(q, fn));
   TRY(check_pool(kp, fn, false));
@@ -188,13 +204,17 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
     return fail(IDX_E_SHAPE, "%s: ld %lld < kb * 8 = %lld", fn, (long long)ld, (long long)tbl->kb * 8);
   if (tbl->rows > 0 && !T) return fail(IDX_E_ARG, "%s: T is NULL", fn);
   if (!aligned(T, 4)) return fail(IDX_E_ALIGN, "%s: T must be 4-byte aligned", fn);
+  TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
   if (tbl->ready) {
     hipError_t e = hipStreamWaitEvent(stream, tbl->ready, 0);
     if (e != hipSuccess) return hip_status(e, "idx_score_sparse_paged: hipStreamWaitEvent");
   }
   if (tbl->rows == 0) return ok();
   idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
-  return hip_status(idxk::launch_score_sparse(qa, kp->pool, kp->num_pages, tbl->phys, tbl->n_kept,
+  uint8_t* fold = static_cast<uint8_t*>(ws);
+  hipError_t e = idxk::launch_fold_query(qa, fold, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(idxk::launch_score_sparse(qa, fold, kp->pool, kp->num_pages, tbl->phys, tbl->n_kept,
                                               tbl->valid_len, tbl->rows, tbl->kb, tbl->schedule, T,
                                               ld, stream), fn);
 }
@@ -218,7 +238,9 @@ idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32
   }
   if (rows == 0) return ok();
   if (!X || !valid || !out) return fail(IDX_E_ARG, "%s: X/valid/out is NULL", fn);
-  return hip_status(idxk::launch_topk(mode, X, ld, valid, nullptr, rows, k, ld, blocks, kb,
+  // widest row the call can see: ld columns, or kb * 8 candidate columns
+  const int64_t width = mode == IDX_COLS_IDENTITY ? ld : (int64_t)kb * idxk::kBlock;
+  return hip_status(idxk::launch_topk(mode, X, ld, valid, nullptr, rows, k, width, blocks, kb,
                                       pos_offset, out, nullptr, stream), fn);
 }
 

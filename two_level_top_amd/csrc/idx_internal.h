@@ -16,6 +16,8 @@ constexpr int kPageBytes = kPage * (kValBytes + kScaleBytes);  // 4352
 constexpr int kBlock = 8;                                      // positions per block
 constexpr int kBlocksPerPage = kPage / kBlock;                 // 8
 constexpr int kUnitBlocks = 64;   // candidate blocks per sparse work unit (512 columns)
+constexpr int kFoldTerms = 16;    // MXFP4 terms of the folded query (one 16-row MFMA block)
+constexpr int kFoldRowBytes = kFoldTerms * (kValBytes + kScaleBytes);  // 1088
 
 // ---------------------------------------------------------------------------
 // launch descriptors
@@ -40,8 +42,12 @@ __device__ __forceinline__ int clamp_req(int r, int num_req) {
   return r < 0 ? 0 : (r >= num_req ? num_req - 1 : r);
 }
 
-hipError_t launch_score_dense(const QueryArgs& q, const PoolArgs& kp, const int32_t* req,
-                              const int32_t* len, float* S, int64_t ld, hipStream_t st);
+// writes kFoldRowBytes per query row (see fold_query.hip)
+hipError_t launch_fold_query(const QueryArgs& q, uint8_t* out, hipStream_t st);
+
+hipError_t launch_score_dense(const QueryArgs& q, const uint8_t* fold, const PoolArgs& kp,
+                              const int32_t* req, const int32_t* len, float* S, int64_t ld,
+                              hipStream_t st);
 
 hipError_t launch_amax8(const float* S, int64_t ld, const int32_t* len, int rows, float* keys,
                         int64_t ldk, int skip, hipStream_t st);
@@ -60,7 +66,8 @@ hipError_t launch_expand(const PoolArgs& kp, const int32_t* req, const int32_t* 
 hipError_t launch_schedule(const int32_t* n_kept, int rows, int kb, void* schedule,
                            hipStream_t st);
 
-hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* pool, int num_pages,
+hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const uint8_t* pool,
+                               int num_pages,
                                const int32_t* phys, const int32_t* n_kept,
                                const int32_t* valid_len, int rows, int kb, const void* schedule,
                                float* T, int64_t ld, hipStream_t st);

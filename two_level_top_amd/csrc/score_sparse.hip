@@ -16,7 +16,9 @@ namespace idxk {
 constexpr int kSparseWaves = 4;
 
 template <int HB>
-__global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q, const uint8_t* __restrict__ pool,
+__global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
+                                                           const uint8_t* __restrict__ fold,
+                                                           const uint8_t* __restrict__ pool,
                                                            int num_pages,
                                                            const int32_t* __restrict__ phys,
                                                            const int32_t* __restrict__ n_kept,
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q, const ui
     const int vl = min(valid_len[row], nk * kBlock);
     const int last = min(first + kUnitBlocks, nk);
     RowFrag<HB> f;
-    load_row(q, row, lane, f);
+    load_row(q, fold, row, lane, f);
     const int32_t* ph = phys + (int64_t)row * kb;
     float* Tr = T + (int64_t)row * ld;
     for (int bb = first; bb < last; bb += 8) {
@@ -67,7 +69,8 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q, const ui
   }
 }
 
-hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* pool, int num_pages,
+hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const uint8_t* pool,
+                               int num_pages,
                                const int32_t* phys, const int32_t* n_kept,
                                const int32_t* valid_len, int rows, int kb, const void* schedule,
                                float* T, int64_t ld, hipStream_t st) {
@@ -78,10 +81,10 @@ hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* pool, int num_
   const int32_t* sched = static_cast<const int32_t*>(schedule);
   const int hb = (q.heads + 15) / 16;
   switch (hb) {
-    case 1: hipLaunchKernelGGL(score_sparse_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, q, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
-    case 2: hipLaunchKernelGGL(score_sparse_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, q, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
-    case 3: hipLaunchKernelGGL(score_sparse_kernel<3>, dim3((unsigned)grid), dim3(256), 0, st, q, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
-    default: hipLaunchKernelGGL(score_sparse_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, q, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
+    case 1: hipLaunchKernelGGL(score_sparse_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
+    case 2: hipLaunchKernelGGL(score_sparse_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
+    case 3: hipLaunchKernelGGL(score_sparse_kernel<3>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
+    default: hipLaunchKernelGGL(score_sparse_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
   }
   return hipGetLastError();
 }

@@ -9,25 +9,45 @@
 //                    positions, -1 past min(k, valid) (same PR, "Level two",
 //                    and the source's own top-512).
 //
-// One workgroup of 1024 threads per row; thread t owns the 32 consecutive
-// elements [32 t, 32 t + 32) of each 32768-element chunk (a whole row of
-// keys or of a consumer's scores is one chunk, held in registers).
-//   1. radix select on order-preserving u32 keys: three LDS histogram passes
-//      (11, 11, 10 bits) find the k-th largest key K and how many elements
-//      equal to K are still needed (`need`);
+// One workgroup per row, of 256, 512 or 1024 threads (the smallest whose
+// registers hold the row: 32 elements per thread), so that several rows run
+// on a CU at once and their barriers and load latency overlap.  A row is
+// processed in chunks of THREADS * 32 elements held in registers (a whole row
+// of block keys or of a consumer's scores is one chunk; longer rows are
+// streamed in chunks); wave w owns the contiguous 2048-element slice
+// [2048 w, 2048 w + 2048) of a chunk and reads it with coalesced 16-byte
+// loads: in step j lane l holds elements 256 j + 4 l .. 256 j + 4 l + 3, all
+// in one block of 8, whose id is loaded once with them.
+// Values become order-preserving u32 keys (-0 folded onto +0); slots past the
+// row's end get key 0, which lies below -inf, so they are never counted as
+// finite, never compare greater than or equal to a threshold, and only ever
+// land in the -inf bin, below every valid element.
+//
+//   1. threshold: the k-th largest key K and `need`, the number of elements
+//      equal to K that are selected.  One histogram pass over the digit
+//      1 + ((key - kmin) >> shift), kmin/kmax being the finite extremes of the
+//      row and shift the smallest one that fits the span in 2046 bins (-inf
+//      gets digit 0, +inf the one above the largest finite digit): one row's
+//      data spreads over the bins, so the LDS atomics rarely collide.  The
+//      keys of the bin holding the k-th largest (a few dozen, typically) are
+//      copied to an LDS list, and up to two more histogram passes (<= 11 bits
+//      each) over that list fix the low bits of K.  A list that would
+//      overflow LDS is refined from the registers instead.
 //   2. ordered compaction: element i is kept iff key > K, or key == K and
-//      fewer than `need` equal keys precede it.  One block scan of the packed
-//      (greater, equal) counts gives every thread its output offset, so the
-//      output comes out in ascending index order with no sort.
+//      fewer than `need` equal keys precede it.  Each wave gets its
+//      predecessors' counts from one 16-entry scan, then walks its slice in
+//      index order with ballots and mbcnt (no further barriers), so the output
+//      comes out in ascending index order with no sort.
 #include "idx_internal.h"
 
 namespace idxk {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kTopkE = 32;
-constexpr int kTopkChunk = kTopkThreads * kTopkE;
-constexpr int kHistBins = 2048;
+constexpr int kTopkMaxWaves = 16;
+constexpr int kTopkSteps = 8;                          // 16-byte loads per lane per chunk
+constexpr int kWaveSlice = kTopkSteps * 256;           // 2048
+constexpr int kBins = 2048;                            // 0: -inf, 1..2046 finite, 2047: +inf
+constexpr uint32_t kPosInf = 0xff800000u;              // order_key(+inf)
+constexpr uint32_t kNegInf = 0x007fffffu;              // order_key(-inf)
 
 enum { MODE_IDENTITY = 0, MODE_BLOCKMAP = 1, MODE_GATHER = 2, MODE_KEYS = 3 };
 
@@ -44,54 +64,64 @@ struct TopkArgs {
   int32_t* n_kept;         // mode 3
 };
 
+constexpr uint32_t kCand = 4096;   // candidate list of the threshold bin
+
 struct TopkShared {
-  uint32_t hist[kHistBins];
-  uint32_t wsum[kTopkWaves];
-  uint32_t wexcl[kTopkWaves];
-  uint32_t total;
-  int32_t digit;
-  int32_t above;
+  uint32_t hist[kBins];
+  uint32_t cand[kCand];
+  uint32_t wred[kTopkMaxWaves][2];
+  uint32_t wcnt[kTopkMaxWaves][2];
+  uint32_t bcast[4];
 };
 
-// Exclusive scan over the workgroup; *total receives the sum.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, TopkShared& sh, uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  uint32_t x = v;
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) sh.wsum[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    const uint32_t s = lane < kTopkWaves ? sh.wsum[lane] : 0u;
-    uint32_t y = s;
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
-    for (int o = 1; o < kTopkWaves; o <<= 1) {
-      const uint32_t z = __shfl_up(y, o, 64);
-      if (lane >= o) y += z;
-    }
-    if (lane < kTopkWaves) sh.wexcl[lane] = y - s;
-    if (lane == kTopkWaves - 1) sh.total = y;
-  }
-  __syncthreads();
-  const uint32_t r = sh.wexcl[wave] + x - v;
-  *total = sh.total;
-  __syncthreads();
-  return r;
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-template <int MODE>
-__device__ __forceinline__ float load_value(const TopkArgs& a, const float* Xr, const int32_t* blk,
-                                            int i) {
-  if (MODE == MODE_GATHER) {
-    int64_t p = (int64_t)blk[i >> 3] * kBlock + (i & 7);
-    if (p < 0 || p >= a.ld) p = 0;   // outside the contract: read something in the row
-    return Xr[p];
+// 4 consecutive values starting at element i (i % 4 == 0) of the row.
+template <int MODE, bool VEC>
+__device__ __forceinline__ void load4(const TopkArgs& a, const float* Xr, const int32_t* blk, int i,
+                                      int n, float (&v)[4]) {
+  if (VEC && i + 3 < n) {
+    int64_t p = i;
+    if (MODE == MODE_GATHER) {
+      p = (int64_t)blk[i >> 3] * kBlock + (i & 7);
+      if (p < 0 || p + 3 >= a.ld) p = 0;   // outside the contract: stay inside the row
+    }
+    const float4 x = *reinterpret_cast<const float4*>(Xr + p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    return;
   }
-  return Xr[i];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int ie = i + e;
+    float x = 0.f;
+    if (ie < n) {
+      int64_t p = ie;
+      if (MODE == MODE_GATHER) {
+        p = (int64_t)blk[ie >> 3] * kBlock + (ie & 7);
+        if (p < 0 || p >= a.ld) p = 0;
+      }
+      x = Xr[p];
+    }
+    v[e] = x;
+  }
 }
 
 template <int MODE>
@@ -100,11 +130,60 @@ __device__ __forceinline__ int32_t map_index(const int32_t* blk, int i) {
   return i;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+// Select the bin holding the rem-th largest of hist[0..kBins) (counted from
+// the top).  Returns the bin and, in *above, the count of the bins above it.
+template <int THREADS>
+__device__ __forceinline__ int find_bin(TopkShared& sh, uint32_t rem, uint32_t* above_out) {
+  constexpr int W = THREADS / 64;
+  constexpr int BPT = kBins / THREADS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t cb[BPT];
+  uint32_t csum = 0u;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    cb[q] = sh.hist[kBins - 1 - BPT * tid - q];
+    csum += cb[q];
+  }
+  uint32_t x = csum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh.wcnt[wave][0] = x;
+  __syncthreads();
+  uint32_t before = 0u;
+#pragma unroll
+  for (int w = 0; w < W; ++w) before += w < wave ? sh.wcnt[w][0] : 0u;
+  const uint32_t above = before + x - csum;
+  if (above < rem && rem <= above + csum) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      if (acc < rem && rem <= acc + cb[q]) {
+        sh.bcast[0] = (uint32_t)(kBins - 1 - BPT * tid - q);
+        sh.bcast[1] = acc;
+      }
+      acc += cb[q];
+    }
+  }
+  __syncthreads();
+  const int b = (int)sh.bcast[0];
+  *above_out = sh.bcast[1];
+  __syncthreads();
+  return b;
+}
+
+// RESIDENT: every row fits one chunk (n <= THREADS * 64), loaded once.
+template <int MODE, bool VEC, int THREADS, bool RESIDENT>
+__global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
+  constexpr int W = THREADS / 64;
+  constexpr int kChunk = W * kWaveSlice;
   __shared__ TopkShared sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   int n;
   if (MODE == MODE_KEYS) {
     const int L = a.len[row];
@@ -123,112 +202,278 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
   const float* Xr = a.X + (int64_t)row * a.ld;
 
   if (n <= k) {  // every column is kept
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? map_index<MODE>(blk, i) + off : pad;
+    for (int i = tid; i < k; i += THREADS) out[i] = i < n ? map_index<MODE>(blk, i) + off : pad;
     if (MODE == MODE_KEYS && tid == 0) a.n_kept[row] = n;
     return;
   }
 
-  uint32_t key[kTopkE];
-  const int nchunks = (n + kTopkChunk - 1) / kTopkChunk;
-  auto load_chunk = [&](int ch) {
-    const int base = ch * kTopkChunk + tid * kTopkE;
+  const int nchunks = RESIDENT ? 1 : (n + kChunk - 1) / kChunk;
+  uint32_t key[kTopkSteps][4];
+  int32_t bid[kTopkSteps];   // block id of step j's elements (modes 1, 2)
+  // element index of key[j][e] in chunk c: c * kChunk + ebase + 256 j + e
+  const int ebase = wave * kWaveSlice + 4 * lane;
+  auto load_chunk = [&](int c) {
 #pragma unroll
-    for (int e = 0; e < kTopkE; ++e) {
-      const int i = base + e;
-      key[e] = i < n ? order_key(load_value<MODE>(a, Xr, blk, i)) : 0u;
+    for (int j = 0; j < kTopkSteps; ++j) {
+      const int i = c * kChunk + ebase + 256 * j;
+      if (MODE == MODE_BLOCKMAP || MODE == MODE_GATHER) bid[j] = i < n ? blk[i >> 3] : 0;
+      float v[4];
+      load4<MODE, VEC>(a, Xr, blk, i, n, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[j][e] = i + e < n ? order_key(v[e]) : 0u;
     }
   };
   if (nchunks == 1) load_chunk(0);
 
-  // ---- 1. radix select of the k-th largest key ----
-  uint32_t prefix = 0u, pmask = 0u;
-  int remaining = k;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
-    for (int b = tid; b < kHistBins; b += kTopkThreads) sh.hist[b] = 0u;
-    __syncthreads();
-    for (int ch = 0; ch < nchunks; ++ch) {
-      if (nchunks > 1) load_chunk(ch);
-      const int base = ch * kTopkChunk + tid * kTopkE;
+  // ---- 1a. finite extremes of the row ----
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int c = 0; c < nchunks; ++c) {
+    if (nchunks > 1) load_chunk(c);
 #pragma unroll
-      for (int e = 0; e < kTopkE; ++e) {
-        if (base + e < n && (key[e] & pmask) == prefix)
-          atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1u);
+    for (int j = 0; j < kTopkSteps; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = key[j][e];
+        const bool fin = x > kNegInf && x < kPosInf;
+        kmin = min(kmin, fin ? x : 0xffffffffu);
+        kmax = max(kmax, fin ? x : 0u);
       }
-    }
-    __syncthreads();
-    // thread t looks at bins 2047 - 2t (higher) and 2046 - 2t
-    const int bh = kHistBins - 1 - 2 * tid, bl = bh - 1;
-    const uint32_t ch_ = sh.hist[bh], cl = sh.hist[bl];
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan(ch_ + cl, sh, &tot);
-    if (above < (uint32_t)remaining && (uint32_t)remaining <= above + ch_ + cl) {
-      if (above + ch_ >= (uint32_t)remaining) {
-        sh.digit = bh;
-        sh.above = (int)above;
-      } else {
-        sh.digit = bl;
-        sh.above = (int)(above + ch_);
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh.digit << shift;
-    pmask |= dmask << shift;
-    remaining -= sh.above;
-    __syncthreads();
   }
-  const uint32_t K = prefix;
-  const uint32_t need = (uint32_t)remaining;
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    sh.wred[wave][0] = kmin;
+    sh.wred[wave][1] = kmax;
+  }
+  if (tid == 0) sh.bcast[2] = 0u;   // candidate list length
+  __syncthreads();
+  kmin = 0xffffffffu;
+  kmax = 0u;
+#pragma unroll
+  for (int w = 0; w < W; ++w) {
+    kmin = min(kmin, sh.wred[w][0]);
+    kmax = max(kmax, sh.wred[w][1]);
+  }
+  if (kmin > kmax) kmin = kmax = 0x80000000u;   // no finite key: any finite stand-in
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  const uint32_t span = kmax - kmin;
+  const int span_bits = span ? 32 - __clz(span) : 0;
+  int shift = span_bits > 11 ? span_bits - 11 : 0;
+  if ((span >> shift) > (uint32_t)(kBins - 3)) ++shift;   // finite digits fit in 0..2045
+  // digit: -inf and the empty slots -> 0, finite x -> 1 + ((x - kmin) >> shift),
+  // +inf -> one above the largest finite digit; monotone in x
+  const uint32_t lo = kmin - (1u << shift), hi = kmax + (1u << shift);
+  auto digit0 = [&](uint32_t x) -> uint32_t {
+    return (min(max(x, lo), hi) - lo) >> shift;
+  };
+  const uint32_t inf_digit = (hi - lo) >> shift;
+
+  // ---- 1b. pass 0: histogram of the digits ----
+  for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    if (nchunks > 1) load_chunk(c);
+#pragma unroll
+    for (int j = 0; j < kTopkSteps; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[digit0(key[j][e])], 1u);
+  }
+  __syncthreads();
+  uint32_t above;
+  const uint32_t bin = (uint32_t)find_bin<THREADS>(sh, (uint32_t)k, &above);
+  uint32_t need = (uint32_t)k - above;
+  uint32_t K;
+  if (bin == 0u) {
+    K = kNegInf;
+  } else if (bin >= inf_digit) {
+    K = kPosInf;
+  } else if (shift == 0) {
+    K = kmin + (bin - 1u);
+  } else {
+    // ---- 1c. the chosen bin's keys: refine their low `shift` bits ----
+    // (an opaque copy of the digit bounds keeps the compiler from holding
+    // every element's digit from pass 0 in registers until here)
+    uint32_t lo_c = __builtin_amdgcn_readfirstlane(lo), hi_c = __builtin_amdgcn_readfirstlane(hi);
+    asm volatile("" : "+s"(lo_c), "+s"(hi_c));
+    auto digit0c = [&](uint32_t x) -> uint32_t { return (min(max(x, lo_c), hi_c) - lo_c) >> shift; };
+    for (int c = 0; c < nchunks; ++c) {
+      if (nchunks > 1) load_chunk(c);
+      // per-lane hit count, one LDS atomic per wave, then in-order slots
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int j = 0; j < kTopkSteps; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine += digit0c(key[j][e]) == bin ? 1u : 0u;
+      uint32_t x = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      const uint32_t wtot = __shfl(x, 63, 64);
+      if (wtot != 0u) {
+        uint32_t base = 0u;
+        if (lane == 0) base = atomicAdd(&sh.bcast[2], wtot);
+        base = __shfl(base, 0, 64);
+        uint32_t pre = base + x - mine;
+#pragma unroll
+        for (int j = 0; j < kTopkSteps; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (digit0c(key[j][e]) == bin) {
+              if (pre < kCand) sh.cand[pre] = key[j][e] - kmin;
+              ++pre;
+            }
+          }
+      }
+    }
+    __syncthreads();
+    const uint32_t m = sh.bcast[2];
+    const bool in_lds = m <= kCand;
+    uint32_t fixed = (bin - 1u) << shift;     // known bits of (key - kmin)
+    int low = shift;                          // bits below `low` still unknown
+    while (low > 0) {
+      const int width = low < 11 ? low : 11;
+      const int sh_lo = low - width;
+      const uint32_t hi_mask = ~((1u << low) - 1u);
+      for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
+      __syncthreads();
+      if (in_lds) {
+        for (uint32_t i = tid; i < m; i += THREADS) {
+          const uint32_t r = sh.cand[i];
+          if ((r & hi_mask) == fixed) atomicAdd(&sh.hist[(r >> sh_lo) & ((1u << width) - 1u)], 1u);
+        }
+      } else {
+        for (int c = 0; c < nchunks; ++c) {
+          if (nchunks > 1) load_chunk(c);
+#pragma unroll
+          for (int j = 0; j < kTopkSteps; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t x = key[j][e];
+              const uint32_t r = x - kmin;
+              if (digit0c(x) == bin && (r & hi_mask) == fixed)
+                atomicAdd(&sh.hist[(r >> sh_lo) & ((1u << width) - 1u)], 1u);
+            }
+        }
+      }
+      __syncthreads();
+      uint32_t ab;
+      const uint32_t d = (uint32_t)find_bin<THREADS>(sh, need, &ab);
+      need -= ab;
+      fixed |= d << sh_lo;
+      low = sh_lo;
+    }
+    K = kmin + fixed;
+  }
 
   // ---- 2. ordered compaction ----
-  uint32_t gt_run = 0u, eq_run = 0u;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    if (nchunks > 1) load_chunk(ch);
-    const int base = ch * kTopkChunk + tid * kTopkE;
+  uint32_t gt_run = 0u, eq_run = 0u;   // block-wide, over previous chunks
+  for (int c = 0; c < nchunks; ++c) {
+    if (nchunks > 1) load_chunk(c);
     uint32_t gt = 0u, eq = 0u;
 #pragma unroll
-    for (int e = 0; e < kTopkE; ++e) {
-      if (base + e < n) {
-        gt += key[e] > K ? 1u : 0u;
-        eq += key[e] == K ? 1u : 0u;
-      }
-    }
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan((gt << 16) | eq, sh, &tot);
-    const uint32_t gt_before = gt_run + (ex >> 16);
-    uint32_t eq_before = eq_run + (ex & 0xffffu);
-    uint32_t o = gt_before + (eq_before < need ? eq_before : need);
+    for (int j = 0; j < kTopkSteps; ++j) {
 #pragma unroll
-    for (int e = 0; e < kTopkE; ++e) {
-      const int i = base + e;
-      if (i < n) {
-        bool take = key[e] > K;
-        if (key[e] == K) {
-          take = eq_before < need;
-          ++eq_before;
-        }
-        if (take) out[o++] = map_index<MODE>(blk, i) + off;
+      for (int e = 0; e < 4; ++e) {
+        gt += (uint32_t)__popcll(__ballot(key[j][e] > K));
+        eq += (uint32_t)__popcll(__ballot(key[j][e] == K));
       }
     }
-    gt_run += tot >> 16;
-    eq_run += tot & 0xffffu;
+    if (lane == 0) {
+      sh.wcnt[wave][0] = gt;
+      sh.wcnt[wave][1] = eq;
+    }
+    __syncthreads();
+    uint32_t gbefore = gt_run, ebefore = eq_run, gtot = 0u, etot = 0u;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const uint32_t g = sh.wcnt[w][0], q = sh.wcnt[w][1];
+      if (w < wave) {
+        gbefore += g;
+        ebefore += q;
+      }
+      gtot += g;
+      etot += q;
+    }
+    // an opaque copy of K keeps the counting ballots above from being reused
+    // (and all held live) here
+    uint32_t Kc = __builtin_amdgcn_readfirstlane(K);
+    asm volatile("" : "+s"(Kc));
+#pragma unroll
+    for (int j = 0; j < kTopkSteps; ++j) {
+      uint64_t G[4], Q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        G[e] = __ballot(key[j][e] > Kc);
+        Q[e] = __ballot(key[j][e] == Kc);
+      }
+      if (((G[0] | G[1] | G[2] | G[3]) | (Q[0] | Q[1] | Q[2] | Q[3])) != 0u) {
+        uint32_t gpre = gbefore, qpre = ebefore;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gpre += lanes_below(G[e]);
+          qpre += lanes_below(Q[e]);
+        }
+        const int ib = c * kChunk + ebase + 256 * j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool g = key[j][e] > Kc, q = key[j][e] == Kc;
+          const int32_t pos = (MODE == MODE_BLOCKMAP || MODE == MODE_GATHER)
+                                  ? bid[j] * kBlock + ((ib + e) & 7) : ib + e;
+          if (g || (q && qpre < need)) out[gpre + min(qpre, need)] = pos + off;
+          gpre += g ? 1u : 0u;
+          qpre += q ? 1u : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gbefore += (uint32_t)__popcll(G[e]);
+          ebefore += (uint32_t)__popcll(Q[e]);
+        }
+      }
+    }
+    gt_run += gtot;
+    eq_run += etot;
+    __syncthreads();
   }
   if (MODE == MODE_KEYS && tid == 0) a.n_kept[row] = k;
 }
 
+template <int MODE, int THREADS, bool RESIDENT>
+static void launch_sized(const TopkArgs& a, int rows, bool vec, hipStream_t st) {
+  if (vec)
+    hipLaunchKernelGGL((topk_kernel<MODE, true, THREADS, RESIDENT>), dim3(rows), dim3(THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL((topk_kernel<MODE, false, THREADS, RESIDENT>), dim3(rows), dim3(THREADS), 0, st, a);
+}
+
+// the workgroup size is chosen from the widest row the call can see
+template <int MODE>
+static void launch_mode(const TopkArgs& a, int rows, int64_t width, bool vec, hipStream_t st) {
+  if (width <= 4 * kWaveSlice)
+    launch_sized<MODE, 256, true>(a, rows, vec, st);
+  else if (width <= 8 * kWaveSlice)
+    launch_sized<MODE, 512, true>(a, rows, vec, st);
+  else if (width <= 16 * kWaveSlice)
+    launch_sized<MODE, 1024, true>(a, rows, vec, st);
+  else
+    launch_sized<MODE, 1024, false>(a, rows, vec, st);
+}
+
 hipError_t launch_topk(int mode, const float* X, int64_t ld, const int32_t* nvalid,
-                       const int32_t* len_for_blocks, int rows, int k, int64_t /*max_cols*/,
+                       const int32_t* len_for_blocks, int rows, int k, int64_t max_cols,
                        const int32_t* blocks, int kb, const int32_t* pos_offset, int32_t* out,
                        int32_t* n_kept, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   TopkArgs a{X, ld, nvalid, len_for_blocks, k, blocks, kb, pos_offset, out, n_kept};
+  // 16-byte loads need 16-byte aligned rows
+  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
   switch (mode) {
-    case MODE_IDENTITY: hipLaunchKernelGGL(topk_kernel<MODE_IDENTITY>, dim3(rows), dim3(kTopkThreads), 0, st, a); break;
-    case MODE_BLOCKMAP: hipLaunchKernelGGL(topk_kernel<MODE_BLOCKMAP>, dim3(rows), dim3(kTopkThreads), 0, st, a); break;
-    case MODE_GATHER: hipLaunchKernelGGL(topk_kernel<MODE_GATHER>, dim3(rows), dim3(kTopkThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL(topk_kernel<MODE_KEYS>, dim3(rows), dim3(kTopkThreads), 0, st, a); break;
+    case MODE_IDENTITY: launch_mode<MODE_IDENTITY>(a, rows, max_cols, vec, st); break;
+    case MODE_BLOCKMAP: launch_mode<MODE_BLOCKMAP>(a, rows, max_cols, vec, st); break;
+    case MODE_GATHER: launch_mode<MODE_GATHER>(a, rows, max_cols, vec, st); break;
+    default: launch_mode<MODE_KEYS>(a, rows, max_cols, vec, st); break;
   }
   return hipGetLastError();
 }
