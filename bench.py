@@ -80,6 +80,31 @@ def algorithmic_work(wl):
     }
 
 
+def measured_traffic(config):
+    """HBM bytes per dense-score launch from the committed counter summary, or None
+    when the summary is for another workload or the kernel sources have changed."""
+    import hashlib
+    if config != "long":
+        return None
+    path = os.path.join(ROOT, "profiles", "score_dense_long_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", " ", "#")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("score_dense.hip", "score_common.h", "idx_internal.h"):
+        h.update(open(os.path.join(ROOT, "two_level_top_amd", "csrc", f), "rb").read())
+    if fields.get("kernel_source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, n_rows):
     """The oracle, as it stands, on n_rows evenly spaced rows of the same chunk."""
     import numpy as np
@@ -102,8 +127,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "tiny"])
-    ap.add_argument("--cpu-rows", type=int, default=64,
+    ap.add_argument("--cpu-rows", type=int, default=192,
                     help="rows of the CPU oracle sample (0 = skip the CPU baseline)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -117,6 +145,15 @@ def main():
     from two_level_top_amd.chunk import Chunk
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n * 4}))
+        return
     wl, desc = workload(args.config)
     print(f"[bench] workload ready: {desc}", file=sys.stderr, flush=True)
     ch = Chunk(wl)
@@ -186,7 +223,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "score_dense",
                      "achieved": round(dense_tflops, 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_FP4_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(args.config)},
         "kernels": kernels,
     }
     if args.cpu_rows > 0:

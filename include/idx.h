@@ -222,7 +222,8 @@ idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_
  * tbl->ready first (if set).
  *   T[r * ld + c] = score'(r, blocks[r][c/8]*8 + c%8) for c < valid_len[r];
  *   T beyond valid_len[r] is not written.
- * q->rows == tbl->rows; ld >= tbl->kb * 8.
+ * q->rows == tbl->rows; ld >= tbl->kb * 8; the pool must be under 4 GiB
+ * (986k pages of 64 positions; else IDX_E_UNSUPPORTED).
  * ws: as for idx_score_dense (IDX_OP_SCORE, q->rows).
  */
 idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,

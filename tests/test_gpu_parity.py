@@ -274,10 +274,11 @@ def test_expand_and_sparse_scores(idx, name):
     assert np.array_equal(host(ch.table.len), wl.lens)
     assert np.array_equal(host(ch.table.req), wl.req)
     sched = host(ch.table.schedule).view(np.int32)
-    units = (n_kept + 63) // 64
-    assert sched[0] == units.sum()
+    U = (wl.kb + 63) // 64
+    assert sched[0] == wl.rows * U
     pairs = sched[4:4 + 2 * sched[0]].reshape(-1, 2)
-    exp = np.array([(r, 64 * u) for r in range(wl.rows) for u in range(units[r])]).reshape(-1, 2)
+    exp = np.array([(r, 64 * u if 64 * u < n_kept[r] else -1)
+                    for r in range(wl.rows) for u in range(U)]).reshape(-1, 2)
     assert np.array_equal(pairs, exp)
     say(f"sparse scores {name}")
     L1 = wl.layers[1]
@@ -393,7 +394,10 @@ def test_prefill_tail(idx):
                     pos_offset=dev(wl.req_start[trows]))
     assert np.array_equal(host(out), host(ch.cons_top[0])[trows])
     sched = host(tail.schedule).view(np.int32)
-    assert sched[0] == ((host(tail.n_kept) + 63) // 64).sum()
+    assert sched[0] == len(trows) * ((wl.kb + 63) // 64)
+    nk = host(tail.n_kept)
+    firsts = sched[4:4 + 2 * sched[0]].reshape(-1, 2)[:, 1]
+    assert ((firsts >= 0).reshape(len(trows), -1).sum(1) == (nk + 63) // 64).all()
 
 
 def test_chunk_prefill_sampled(idx):
@@ -401,3 +405,30 @@ def test_chunk_prefill_sampled(idx):
     say("chunk prefill 2048 x 65536 (sampled rows)")
     ch = _run_chunk(idx, wl)
     _check_chunk(wl, ch, np.array([0, 5, 1000, 2047]), 2)
+
+
+def test_chunk_long_sampled(idx):
+    """The benchmarked chunk itself: 16384 rows at 262144-position context,
+    source + 4 consumers, launched exactly as bench.py launches it; sampled
+    rows checked against the oracle."""
+    wl = workloads.long_chunk()
+    say("chunk long 16384 x 262144, source + 4 consumers (sampled rows)")
+    ch = _run_chunk(idx, wl)
+    _check_chunk(wl, ch, np.array([0, 1, 2, 4095, 8192, 12345, 16382, 16383]), None)
+
+
+def test_chunk_mixed_full(idx):
+    """The mixed batch at full size: 8 prefill requests and 256 decode rows
+    up to 262144 context, duplicated K records, plus its tail table."""
+    import two_level_top_amd as t
+    wl = workloads.mixed()
+    say(f"chunk mixed full (rows {wl.rows}, pages {wl.num_pages})")
+    ch = _run_chunk(idx, wl)
+    starts = np.concatenate([[0], np.cumsum(wl.rows_per_req)])
+    rows = np.unique(np.concatenate([starts[:8], starts[1:9] - 1, starts[8] + np.arange(0, 256, 37)]))
+    _check_chunk(wl, ch, rows, None)
+    trows = oracle.tail_rows(wl.rows_per_req, wl.tail_len)
+    tail = t.Table(len(trows), wl.kb)
+    t.idx_prefill_tail(ch.table, wl.rows_per_req, wl.tail_len, tail)
+    for name in ("blocks", "n_kept", "phys", "valid_len", "len", "req"):
+        assert np.array_equal(host(getattr(tail, name)), host(getattr(ch.table, name))[trows]), name

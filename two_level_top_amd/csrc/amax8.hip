@@ -4,10 +4,11 @@
 //   keys[r][i] = max(S[r][8i .. 8i+7]) for i < nblk - 1, keys[r][nblk-1] = +inf,
 //   rows with nblk <= skip untouched.
 //
-// Pure HBM stream: each thread owns 4 keys 256 apart, so every load
-// instruction of a wave covers 64 consecutive 32-byte blocks (2 KB).  The
-// scores are read once (nontemporal: they are not reused) and the newest
-// block is never read (its key is +inf whatever it holds).
+// Pure HBM stream: each thread owns 4 keys 256 apart (8 loads of 16 bytes in
+// flight), so every load instruction of a wave covers 64 consecutive 32-byte
+// blocks (2 KB).  The newest block is never read (its key is +inf whatever it
+// holds).  (Measured on MI355X: 4 keys per thread with ordinary cached loads
+// streamed fastest; 8 keys, 512 threads or nontemporal loads were slower.)
 #include "idx_internal.h"
 
 namespace idxk {
@@ -34,8 +35,8 @@ __global__ __launch_bounds__(kAmaxThreads) void amax8_kernel(const float* __rest
   for (int j = 0; j < kAmaxItems; ++j) {
     const int i = first + threadIdx.x + j * kAmaxThreads;
     if (i < nblk - 1) {
-      v[j][0] = __builtin_nontemporal_load(in + 2 * i);
-      v[j][1] = __builtin_nontemporal_load(in + 2 * i + 1);
+      v[j][0] = in[2 * i];
+      v[j][1] = in[2 * i + 1];
     }
   }
 #pragma unroll

@@ -10,9 +10,11 @@
 // The newest block is always kept and sorts last, so the only partial block
 // is the last candidate and the valid columns are exactly [0, valid_len).
 //
-// Work list layout (int32): [0] unit count, [1..3] unused, then one
-// (row, first block) pair per unit of 64 candidate blocks, rows in order.  It
-// is built by a single workgroup with a block scan, so it is deterministic.
+// Work list layout (int32): [0] entry count = rows * U, [1..3] unused, then
+// U = ceil(kb / 64) (row, first block) entries per row, row-major: entry
+// (r, u) is (r, 64 u) when the row keeps more than 64 u blocks, else (r, -1),
+// an empty unit the scorer skips.  Every entry is written by the thread that
+// owns it, so building the list costs one pass and is deterministic.
 #include "idx_internal.h"
 
 namespace idxk {
@@ -49,48 +51,17 @@ __global__ __launch_bounds__(256) void expand_kernel(PoolArgs kp, const int32_t*
   }
 }
 
-constexpr int kSchedThreads = 1024;
-
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* __restrict__ n_kept,
-                                                                 int rows, int kb,
-                                                                 int32_t* __restrict__ sched) {
-  __shared__ int32_t wsum[kSchedThreads / 64];
-  __shared__ int32_t wexcl[kSchedThreads / 64 + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int running = 0;
-  for (int base = 0; base < rows; base += kSchedThreads) {
-    const int r = base + threadIdx.x;
-    const int nk = r < rows ? min(max(n_kept[r], 0), kb) : 0;
-    const int units = (nk + kUnitBlocks - 1) / kUnitBlocks;
-    int x = units;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-      const int s = lane < kSchedThreads / 64 ? wsum[lane] : 0;
-      int y = s;
-#pragma unroll
-      for (int o = 1; o < kSchedThreads / 64; o <<= 1) {
-        const int z = __shfl_up(y, o, 64);
-        if (lane >= o) y += z;
-      }
-      if (lane < kSchedThreads / 64) wexcl[lane] = y - s;
-      if (lane == kSchedThreads / 64 - 1) wexcl[kSchedThreads / 64] = y;
-    }
-    __syncthreads();
-    const int first = running + wexcl[wave] + x - units;
-    for (int u = 0; u < units; ++u) {
-      sched[4 + 2 * (first + u)] = r;
-      sched[5 + 2 * (first + u)] = u * kUnitBlocks;
-    }
-    running += wexcl[kSchedThreads / 64];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) sched[0] = running;
+// entries of rows [0, rows): one thread per entry
+__global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict__ n_kept, int rows,
+                                                       int kb, int32_t* __restrict__ sched) {
+  const int units = (kb + kUnitBlocks - 1) / kUnitBlocks;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e == 0) sched[0] = rows * units;
+  if (e >= (int64_t)rows * units) return;
+  const int r = (int)(e / units), u = (int)(e % units);
+  const int nk = min(max(n_kept[r], 0), kb);
+  sched[4 + 2 * e] = r;
+  sched[5 + 2 * e] = u * kUnitBlocks < nk ? u * kUnitBlocks : -1;
 }
 
 __global__ __launch_bounds__(256) void tail_gather_kernel(
@@ -122,7 +93,10 @@ size_t schedule_bytes(int rows, int kb) {
 
 hipError_t launch_schedule(const int32_t* n_kept, int rows, int kb, void* schedule,
                            hipStream_t st) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, n_kept, rows, kb,
+  const int64_t entries = (int64_t)(rows > 0 ? rows : 0) * ((kb + kUnitBlocks - 1) / kUnitBlocks);
+  const int64_t grid = entries > 0 ? (entries + 255) / 256 : 1;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(schedule_kernel, dim3((unsigned)grid), dim3(256), 0, st, n_kept, rows, kb,
                      static_cast<int32_t*>(schedule));
   return hipGetLastError();
 }

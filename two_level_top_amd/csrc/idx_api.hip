@@ -202,6 +202,8 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
   if (q->rows != tbl->rows) return fail(IDX_E_SHAPE, "%s: query rows %d != table rows %d", fn, q->rows, tbl->rows);
   if (ld < (int64_t)tbl->kb * idxk::kBlock)
     return fail(IDX_E_SHAPE, "%s: ld %lld < kb * 8 = %lld", fn, (long long)ld, (long long)tbl->kb * 8);
+  if ((int64_t)kp->num_pages * idxk::kPageBytes > 0xffffffffLL)
+    return fail(IDX_E_UNSUPPORTED, "%s: pool of %d pages exceeds 4 GiB", fn, kp->num_pages);
   if (tbl->rows > 0 && !T) return fail(IDX_E_ARG, "%s: T is NULL", fn);
   if (!aligned(T, 4)) return fail(IDX_E_ALIGN, "%s: T must be 4-byte aligned", fn);
   TRY(check_score_ws(ws, ws_bytes, q->rows, fn));

@@ -6,14 +6,46 @@
 //
 // The work list (built by idx_expand_candidates) holds one unit per 64
 // candidate blocks of a row.  A wave takes a unit, keeps the row's query in
-// registers and walks 2 candidate blocks (16 positions) per MFMA tile: lane l
-// gathers 16 bytes of position (l % 8) of block (l % 16) / 8 -- each block is
-// 512 contiguous value bytes and 32 scale bytes of one pool page.
+// registers, loads the unit's 64 pool-block ids once (one per lane) and walks
+// 2 candidate blocks (16 positions) per MFMA tile, 4 tiles per group with the
+// next group's K prefetched: lane l gathers 16 bytes of position (l % 8) of
+// block (l % 16) / 8 -- each block is 512 contiguous value bytes and 32
+// contiguous scale bytes of one pool page.
 #include "score_common.h"
 
 namespace idxk {
 
 constexpr int kSparseWaves = 4;
+
+// K operands of 4 tiles (8 candidate blocks) of one unit.
+struct GroupOps {
+  uint4 b[4];
+  int sb[4];
+};
+
+// Lane l needs position (l % 8) of block 2 t + (l % 16) / 8 of the group;
+// the blocks' pool ids come from the unit's id vector `pbv` (lane i holds
+// candidate block first + i) by readlane, so no per-tile address load is
+// on the critical path.  Blocks past `nblk` (the unit's end) read block 0 of
+// the unit and are never stored.
+// `bov` holds, in lane i, the byte offset of candidate block first + i's
+// values in the pool (its scales sit at bov + 4096 - 7 * 64 * (block in page),
+// folded into `sov`).
+__device__ __forceinline__ void load_group(const uint8_t* pool, uint32_t bov, uint32_t sov, int g,
+                                           int nblk, int lane, GroupOps& o) {
+  const int slot = lane & 7;
+  const bool half = (lane >> 3) & 1;
+  const uint32_t voff = slot * kValBytes + (lane >> 4) * 16;
+  const uint32_t soff = slot * kScaleBytes + (lane >> 4);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i0 = min(8 * g + 2 * t, nblk - 1), i1 = min(8 * g + 2 * t + 1, nblk - 1);
+    const uint32_t v0 = __builtin_amdgcn_readlane(bov, i0), v1 = __builtin_amdgcn_readlane(bov, i1);
+    const uint32_t s0 = __builtin_amdgcn_readlane(sov, i0), s1 = __builtin_amdgcn_readlane(sov, i1);
+    o.b[t] = *reinterpret_cast<const uint4*>(pool + (half ? v1 : v0) + voff);
+    o.sb[t] = pool[(half ? s1 : s0) + soff];
+  }
+}
 
 template <int HB>
 __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
@@ -26,45 +58,41 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
                                                            int kb, const int32_t* __restrict__ sched,
                                                            float* __restrict__ T, int64_t ld) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int max_units = q.rows * ((kb + kUnitBlocks - 1) / kUnitBlocks);
   const int nunits = min(sched[0], max_units);
   for (int u = blockIdx.x * kSparseWaves + wave; u < nunits; u += gridDim.x * kSparseWaves) {
-    const int row = sched[4 + 2 * u];
-    const int first = sched[5 + 2 * u];
+    const int row = __builtin_amdgcn_readfirstlane(sched[4 + 2 * u]);
+    const int first = __builtin_amdgcn_readfirstlane(sched[5 + 2 * u]);
     if (row < 0 || row >= q.rows || first < 0) continue;   // not a work list this table built
-    const int nk = min(max(n_kept[row], 0), kb);
-    const int vl = min(valid_len[row], nk * kBlock);
-    const int last = min(first + kUnitBlocks, nk);
+    const int nk = __builtin_amdgcn_readfirstlane(min(max(n_kept[row], 0), kb));
+    const int vl = __builtin_amdgcn_readfirstlane(min(valid_len[row], nk * kBlock));
+    const int nblk = min(kUnitBlocks, nk - first);   // candidate blocks of this unit
+    if (nblk <= 0) continue;
     RowFrag<HB> f;
     load_row(q, fold, row, lane, f);
-    const int32_t* ph = phys + (int64_t)row * kb;
-    float* Tr = T + (int64_t)row * ld;
-    for (int bb = first; bb < last; bb += 8) {
+    // byte offsets of this lane's candidate block (pools are < 4 GiB here)
+    const int pb = phys[(int64_t)row * kb + first + min(lane, nblk - 1)];
+    const uint32_t pgo = (uint32_t)clamp_page(pb >> 3, num_pages) * (uint32_t)kPageBytes;
+    const uint32_t bov = pgo + (uint32_t)(pb & 7) * (kBlock * kValBytes);
+    const uint32_t sov = pgo + kPageValBytes + (uint32_t)(pb & 7) * (kBlock * kScaleBytes);
+    float* Tr = T + (int64_t)row * ld + first * kBlock;
+    const int ngroups = (nblk + 7) / 8;
+    GroupOps cur, nxt;
+    load_group(pool, bov, sov, 0, nblk, lane, cur);
+    for (int g = 0; g < ngroups; ++g) {
+      load_group(pool, bov, sov, min(g + 1, ngroups - 1), nblk, lane, nxt);
       float p[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int blk0 = bb + 2 * t;
-        if (blk0 < last) {
-          const int bi = blk0 + ((lane & 15) >> 3);
-          uint4 b = make_uint4(0u, 0u, 0u, 0u);
-          int sb = 127;
-          if (bi < last) {
-            const int pb = ph[bi];
-            const int64_t page = clamp_page(pb >> 3, num_pages);
-            const int slot = (pb & 7) * kBlock + (lane & 7);
-            const uint8_t* pg = pool + page * kPageBytes;
-            b = *reinterpret_cast<const uint4*>(pg + slot * kValBytes + (lane >> 4) * 16);
-            sb = pg[kPageValBytes + slot * kScaleBytes + (lane >> 4)];
-          }
-          p[t] = tile_partial<HB>(f, b, sb);
-        } else {
-          p[t] = 0.f;
-        }
+        v4f acc[HB + 1];
+        tile_mfma<HB>(f, cur.b[t], cur.sb[t], acc);
+        p[t] = tile_epilogue<HB>(f, acc);
       }
       const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
-      const int c = bb * kBlock + lane;
-      if (c < vl) Tr[c] = tot;
+      const int c = g * 64 + lane;   // column within the unit
+      if (first * kBlock + c < vl && c < nblk * kBlock) Tr[c] = tot;
+      cur = nxt;
     }
   }
 }
