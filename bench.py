@@ -184,17 +184,18 @@ def main():
 
     t_dense = avg("dense<", "dense>")
     t_amax = avg("amax8<", "amax8>")
-    t_tkb = avg("amax8>", "topk_blocks>")
+    t_tkb = avg("topk_blocks<", "topk_blocks>")
     t_exp = avg("topk_blocks>", "expand>")
     t_src = avg("source_topk<", "source_topk>")
     t_sp = [avg(f"sparse{i}<", f"sparse{i}>") for i in range(ncons)]
     t_tr = [avg(f"sparse{i}>", f"topk_rows{i}>") for i in range(ncons)]
     dense_tflops = work["dense_flops"] / (t_dense * 1e-3) / 1e12
+    dense_name = "score_dense_keys" if ch.fused_keys else "score_dense"
     kernels = {
-        "score_dense": {"ms": round(t_dense, 4), "TFLOP/s": round(dense_tflops, 1),
-                        "frac_fp4_peak": round(dense_tflops / PEAK_FP4_TFLOPS, 4)},
-        "amax8_varlen": {"ms": round(t_amax, 4),
-                         "GB/s": round(work["amax8_bytes"] / (t_amax * 1e-3) / 1e9, 1)},
+        dense_name: {"ms": round(t_dense, 4), "TFLOP/s": round(dense_tflops, 1),
+                     "frac_fp4_peak": round(dense_tflops / PEAK_FP4_TFLOPS, 4)},
+        **({} if ch.fused_keys else {"amax8_varlen": {
+            "ms": round(t_amax, 4), "GB/s": round(work["amax8_bytes"] / (t_amax * 1e-3) / 1e9, 1)}}),
         "topk_blocks": {"ms": round(t_tkb, 4),
                         "GB/s": round(work["topk_blocks_bytes"] / (t_tkb * 1e-3) / 1e9, 1)},
         "expand_candidates": {"ms": round(t_exp, 4)},
@@ -220,7 +221,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "rows": wl.rows, "heads": wl.heads, "kb": wl.kb,
                    "topk": wl.kc, "consumers": ncons},
-        "roofline": {"bound": "mfma", "kernel": "score_dense",
+        "roofline": {"bound": "mfma", "kernel": dense_name,
                      "achieved": round(dense_tflops, 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_FP4_TFLOPS, 4),
                      "traffic": measured_traffic(args.config)},

@@ -79,7 +79,8 @@ const char* idx_version(void);
  *   vals   u8  [rows][heads][64]   packed e2m1 codes
  *   scales u8  [rows][heads][4]    ue8m0 scales
  *   w      f32 [rows][heads]       head weights (already folded upstream)
- * 1 <= heads <= 64 (64 in the model; 8 in small tests); dim must be 128. */
+ * 1 <= heads <= 64 (64 in the model; 8 in small tests); dim must be 128.
+ * vals 16-byte, scales and w 4-byte aligned (IDX_E_ALIGN otherwise). */
 typedef struct {
   const uint8_t* vals;
   const uint8_t* scales;
@@ -166,8 +167,8 @@ size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k);
  * source scores in full; vLLM indexer page: fp8_fp4_mqa_logits over
  * [ks, ke) of each row.
  *   S[r * ld + p] = score(r, p) for p < len[r]; S beyond len[r] is not written.
- * q->rows == rows->rows; ld >= max len (not checked: device data) and ld >= 1;
- * S must be 4-byte aligned.
+ * q->rows == rows->rows; ld >= max len (not checked: device data) and
+ * 1 <= ld <= 2^29; S must be 4-byte aligned.
  * ws: idx_workspace_bytes(IDX_OP_SCORE, q->rows, 0, 0) device bytes, 16-byte
  * aligned; the call first writes there each row's weight-folded query
  * sum_h (w_h/2) q_h as 16 MXFP4 terms (exact), which lets the kernel use
@@ -188,6 +189,24 @@ idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_ro
  */
 idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int32_t rows,
                             float* keys, int64_t ldk, int32_t skip_le_blocks, hipStream_t stream);
+
+/*
+ * idx_score_dense_keys -- the fused source pass: idx_score_dense and
+ * idx_amax8_varlen in one kernel, so the block keys come from the scores
+ * while they are still on chip instead of re-reading S (the prefill PR's
+ * stated follow-up: block amax folded into the score kernel).
+ * S is written exactly as by idx_score_dense(q, kp, rows, S, ld, ws, ...);
+ * keys exactly as by idx_amax8_varlen(S, ld, rows->len, rows->rows, keys,
+ * ldk, skip_le_blocks) on that S (same fp32 values, newest block +inf, rows
+ * with nblk <= skip_le_blocks untouched).
+ * Arguments and errors: the union of the two calls' (ld % 8 == 0, ldk >= 1,
+ * skip_le_blocks >= 0, keys 4-byte aligned and non-NULL); S needs only 4-byte
+ * alignment.  Same workspace as idx_score_dense.
+ */
+idx_status idx_score_dense_keys(const idx_query* q, const idx_kpool* kp, const idx_rows* rows,
+                                float* S, int64_t ld, float* keys, int64_t ldk,
+                                int32_t skip_le_blocks, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
 
 /*
  * idx_topk_blocks -- the kb best blocks of each row (prefill PR, "Level one":

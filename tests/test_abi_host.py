@@ -49,6 +49,7 @@ def lib():
 
 FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
 FAKE_ODD = ctypes.c_void_p(0x100004)
+FAKE_ODD2 = ctypes.c_void_p(0x100002)  # not even 4-byte aligned
 
 
 def _err(lib):
@@ -105,6 +106,25 @@ def test_score_validation(lib):
     assert lib.idx_score_sparse_paged(P(q), P(kp), P(tbl), FAKE, 64, FAKE, W, None) == -3     # ld
     assert lib.idx_score_sparse_paged(P(q), P(kp), P(tbl), FAKE, 128, None, 0, None) == -6   # workspace
     assert lib.idx_expand_candidates(P(kp), P(r3), P(tbl), None) == -3
+
+
+def test_score_dense_keys_validation(lib):
+    t, q, kp, rows, tbl = _structs()
+    P = ctypes.byref
+    W = 1 << 20
+    f = lib.idx_score_dense_keys
+    assert f(P(q), P(kp), P(rows), FAKE, 1024, None, 128, 0, FAKE, W, None) == -1     # keys NULL
+    assert "keys" in _err(lib)
+    assert f(P(q), P(kp), P(rows), FAKE, 1020, FAKE, 128, 0, FAKE, W, None) == -2     # ld % 8
+    assert f(P(q), P(kp), P(rows), FAKE, 1024, FAKE, 0, 0, FAKE, W, None) == -1       # ldk < 1
+    assert f(P(q), P(kp), P(rows), FAKE, 1024, FAKE, 128, -1, FAKE, W, None) == -1    # skip < 0
+    assert f(P(q), P(kp), P(rows), FAKE, 1024, FAKE_ODD2, 128, 0, FAKE, W, None) == -2  # keys align
+    assert f(P(q), P(kp), P(rows), FAKE, 1024, FAKE, 128, 0, FAKE, 100, None) == -6   # workspace
+    bad = t._Query(FAKE, FAKE, FAKE, 4, 64, 64)
+    assert f(P(bad), P(kp), P(rows), FAKE, 1024, FAKE, 128, 0, FAKE, W, None) == -4   # dim
+    r0 = t._Rows(FAKE, FAKE, None, 0)
+    q0 = t._Query(FAKE, FAKE, FAKE, 0, 64, 128)
+    assert f(P(q0), P(kp), P(r0), None, 1024, None, 128, 0, None, 0, None) == 0       # nothing to do
 
 
 def test_tail_validation(lib):

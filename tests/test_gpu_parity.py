@@ -153,6 +153,123 @@ def test_amax8_bitexact(idx, width, kb):
             assert (kg[r, m:] == -7.0).all(), f"row {r} written past nblk"
 
 
+def _e2m1_table():
+    return np.array([oracle.e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def _dequant(codes, scales):
+    """[..., 64] code bytes + [..., 4] ue8m0 bytes -> [..., 128] fp64 values."""
+    tab = _e2m1_table()
+    lo, hi = codes & 15, codes >> 4
+    v = np.stack([tab[lo], tab[hi]], axis=-1).reshape(*codes.shape[:-1], 128)
+    sc = np.exp2(scales.astype(np.float64) - 127.0)
+    return v * np.repeat(sc, 32, axis=-1)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged24", "long"])
+def test_fold_workspace(idx, name):
+    """The score calls' workspace holds sum_h (w_h/2) q_h as 16 MXFP4 terms:
+    their sum equals the fp64 fold up to the greedy split's residual (each
+    term shrinks a group's largest residual at least 3-fold)."""
+    from two_level_top_amd.chunk import Chunk
+    if name == "long":
+        wl = workloads.long_chunk(n_consumers=0)
+        rows = np.array([0, 1, 2, 3, 8191, 16380, 16381, 16382, 16383])
+    else:
+        wl, _ = _fused_case("tiny" if name == "tiny" else "ragged64")
+        if name == "ragged24":
+            wl, _ = _fused_case("ragged24")
+        rows = np.arange(wl.rows)
+    say(f"fold workspace {name}")
+    ch = Chunk(wl, n_consumers=0)
+    L = wl.layers[0]
+    q = idx.Query(dev(L.qv), dev(L.qs), dev(L.w))
+    S = torch.empty((wl.rows, wl.ld), dtype=torch.float32, device="cuda")
+    ws = idx.score_workspace(wl.rows)
+    idx.idx_score_dense(q, ch.kp, ch.rows, S, ws=ws)
+    fold = host(ws)[: wl.rows * 1088].reshape(wl.rows, 1088)[rows]
+    terms = _dequant(fold[:, :1024].reshape(-1, 16, 64), fold[:, 1024:].reshape(-1, 16, 4))
+    got = terms.sum(axis=1)
+    qv = _dequant(L.qv[rows], L.qs[rows])                       # [n, H, 128]
+    want = np.einsum("nh,nhd->nd", 0.5 * L.w[rows].astype(np.float64), qv)
+    gmax = np.abs(want).reshape(len(rows), 4, 32).max(axis=2)   # per scale group
+    bound = np.repeat(gmax, 32, axis=1) * 3.0 ** -16
+    err = np.abs(got - want)
+    assert (err <= bound).all(), f"fold residual {err.max():.3g} above the 16-term bound"
+
+
+# ---------------------------------------------------------------------------
+# idx_score_dense_keys: the fused source pass
+# ---------------------------------------------------------------------------
+
+def _fused_case(name):
+    if name == "tiny":
+        return workloads.tiny(), None
+    if name.startswith("ragged"):
+        heads = int(name[6:])
+        if heads == 24:
+            return workloads.custom("ragged", 55, 24, 8, 8, [1000, 77, 5], [2, 1, 2],
+                                    [[990, 1000], [77], [0, 5]], n_layers=1), None
+        # keyed and keep-all rows (kb = 8 blocks), an empty row, partial newest blocks
+        return workloads.custom("ragged", 31 + heads, heads, 8, 8, [1000, 77, 5, 300, 2100],
+                                [5, 1, 2, 3, 4],
+                                [[990, 996, 997, 998, 1000], [77], [0, 5], [1, 250, 300],
+                                 [1, 64, 1500, 2100]], n_layers=1), None
+    if name == "decode":
+        return workloads.decode(n_consumers=0), None
+    if name == "prefill":
+        return workloads.prefill(n_consumers=0), [0, 1, 2, 777, 1024, 2045, 2046, 2047]
+    return workloads.long_chunk(n_consumers=0), [0, 1, 8191, 16383]
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged64", "ragged8", "decode", "prefill", "long"])
+@pytest.mark.parametrize("skip", ["kb", 0])
+def test_dense_keys_fused(idx, name, skip):
+    """Keys of the fused pass equal idx_amax8_varlen on the same S (every row,
+    bit for bit as numbers), S equals idx_score_dense's bit for bit, and S is
+    within tolerance of the oracle on sampled rows."""
+    from two_level_top_amd.chunk import Chunk
+    if name == "long" and skip == 0:
+        pytest.skip("the long chunk runs once, with skip = kb as benchmarked")
+    wl, sample = _fused_case(name)
+    sk = wl.kb if skip == "kb" else 0
+    say(f"dense keys fused {name} skip={sk}")
+    ch = Chunk(wl, n_consumers=0)
+    L = wl.layers[0]
+    q = idx.Query(dev(L.qv), dev(L.qs), dev(L.w))
+    S = torch.full((wl.rows, wl.ld), float("nan"), dtype=torch.float32, device="cuda")
+    keys = torch.full((wl.rows, wl.ldk), -7.0, dtype=torch.float32, device="cuda")
+    idx.idx_score_dense_keys(q, ch.kp, ch.rows, S, keys, skip_le_blocks=sk)
+    ref_keys = torch.full_like(keys, -7.0)
+    idx.idx_amax8_varlen(S, ch.rows.len, ref_keys, skip_le_blocks=sk)
+    torch.cuda.synchronize()
+    assert bool((keys == ref_keys).all()), "fused keys differ from idx_amax8_varlen on the same S"
+    S2 = torch.full_like(S, float("nan"))
+    idx.idx_score_dense(q, ch.kp, ch.rows, S2)
+    same = (S == S2) | (torch.isnan(S) & torch.isnan(S2))
+    assert bool(same.all()), "fused scores differ from idx_score_dense"
+    del S2
+    rows = np.arange(wl.rows) if sample is None else np.asarray(sample)
+    ref = oracle.dense_scores(L.qv, L.qs, L.w, wl.req, wl.lens, wl.pool, wl.page_table,
+                              row_ids=rows, ld=wl.ld)
+    Sg = host(S[torch.from_numpy(rows).cuda()])
+    valid = np.arange(wl.ld)[None, :] < wl.lens[rows][:, None]
+    assert_close(Sg, ref, valid, f"{name} fused dense")
+    ko = oracle.block_keys(ref, wl.lens[rows], sk, ldk=wl.ldk)
+    kg = host(keys[torch.from_numpy(rows).cuda()])
+    nblk = oracle.nblocks(wl.lens[rows])
+    for i, r in enumerate(rows):
+        m = int(nblk[i])
+        if m <= sk:
+            assert (kg[i] == -7.0).all(), f"row {r}: keys written for a keep-all row"
+            continue
+        assert np.isposinf(kg[i, m - 1]), f"row {r}: newest block key is not +inf"
+        assert (kg[i, m:] == -7.0).all(), f"row {r}: keys written past nblk"
+        g, o = kg[i, :m - 1].astype(np.float64), ko[i, :m - 1].astype(np.float64)
+        bad = np.abs(g - o) > ATOL + RTOL * np.abs(o)
+        assert not bad.any(), f"row {r}: {bad.sum()} block keys outside tolerance of the oracle's"
+
+
 # ---------------------------------------------------------------------------
 # idx_topk_blocks (bit-exact)
 # ---------------------------------------------------------------------------

@@ -5,7 +5,7 @@ current HIP stream out to the C ABI of include/idx.h.  Every step runs in the
 library's HIP kernels; there is no fallback.  If libidx.so has not been built
 (``python -c "import __graft_entry__ as g; g.build()"``), every call raises.
 
-Names follow the C ABI: idx_score_dense, idx_amax8_varlen, idx_topk_blocks,
+Names follow the C ABI: idx_score_dense, idx_score_dense_keys, idx_amax8_varlen, idx_topk_blocks,
 idx_expand_candidates, idx_score_sparse_paged, idx_topk_rows,
 idx_prefill_tail.
 """
@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "IdxError", "Query", "KPool", "Rows", "Table", "load",
-    "idx_score_dense", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
+    "idx_score_dense", "idx_score_dense_keys", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
     "idx_score_sparse_paged", "idx_topk_rows", "idx_prefill_tail", "idx_workspace_bytes",
     "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table", "score_workspace",
 ]
@@ -77,6 +77,7 @@ def load():
     sig = {
         "idx_score_dense": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_amax8_varlen": [_P, _I64, _P, _I32, _P, _I64, _I32, _P],
+        "idx_score_dense_keys": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P, _I64, _I32, _P, ctypes.c_size_t, _P],
         "idx_topk_blocks": [_P, _I64, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
         "idx_expand_candidates": [ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), ctypes.POINTER(_Table), _P],
         "idx_score_sparse_paged": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P, ctypes.c_size_t, _P],
@@ -271,6 +272,17 @@ def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, ws=None, s
     _check(load().idx_score_dense(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
                                   _ptr(S), S.stride(0), _ptr(ws), ws.numel(), _stream(stream)),
            "idx_score_dense")
+
+
+def idx_score_dense_keys(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, keys: torch.Tensor,
+                         skip_le_blocks: int = 0, ws=None, stream=None):
+    _req(S, torch.float32, "S"); _req(keys, torch.float32, "keys")
+    ws = _score_ws(ws, q.rows, S.device, stream)
+    q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
+    _check(load().idx_score_dense_keys(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
+                                       _ptr(S), S.stride(0), _ptr(keys), keys.stride(0),
+                                       int(skip_le_blocks), _ptr(ws), ws.numel(), _stream(stream)),
+           "idx_score_dense_keys")
 
 
 def idx_amax8_varlen(S, lens, keys, skip_le_blocks: int = 0, stream=None):

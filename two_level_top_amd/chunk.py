@@ -4,9 +4,11 @@ Stream choreography of the publish/select handoff (sglang PR "dsv4.1:
 candidate indexer library", Summary and review; vLLM decode page,
 CandidateOverlap fork/join; prefill PR, "Level one"):
 
-  main stream   idx_score_dense (source) -> event "scores ready"
-  side stream   waits "scores ready"; idx_amax8_varlen, idx_topk_blocks,
-                idx_expand_candidates, which records table.ready
+  main stream   idx_score_dense_keys (source scores and their block keys in
+                one pass; or idx_score_dense) -> event "scores ready"
+  side stream   waits "scores ready"; (idx_amax8_varlen when the keys were
+                not fused,) idx_topk_blocks, idx_expand_candidates, which
+                records table.ready
   main stream   source's own top-k (waits table.ready when it reads the
                 table), then per consumer idx_score_sparse_paged (waits
                 table.ready inside the call) and idx_topk_rows.
@@ -27,8 +29,9 @@ from __future__ import annotations
 import torch
 
 from . import (COLS_BLOCKMAP, COLS_GATHER, COLS_IDENTITY, KPool, Query, Rows, Table,
-               idx_amax8_varlen, idx_expand_candidates, idx_score_dense, idx_score_sparse_paged,
-               idx_topk_blocks, idx_topk_rows, score_workspace, stream_wait_table)
+               idx_amax8_varlen, idx_expand_candidates, idx_score_dense, idx_score_dense_keys,
+               idx_score_sparse_paged, idx_topk_blocks, idx_topk_rows, score_workspace,
+               stream_wait_table)
 
 
 def _dev(a, dtype, device):
@@ -39,8 +42,9 @@ class Chunk:
     """Device copies of a workload (see the workloads package) and its buffers."""
 
     def __init__(self, wl, device="cuda", n_consumers=None, k_source=None, with_offset=True,
-                 share_T=True):
+                 share_T=True, fused_keys=True):
         self.wl = wl
+        self.fused_keys = fused_keys
         self.device = device
         self.R, self.kb, self.kc = wl.rows, wl.kb, wl.kc
         self.k_src = wl.kc if k_source is None else k_source
@@ -73,7 +77,11 @@ class Chunk:
     # -- the source layer ---------------------------------------------------
     def score_source(self, stream=None):
         self._mark("dense<")
-        idx_score_dense(self.queries[0], self.kp, self.rows, self.S, ws=self.ws, stream=stream)
+        if self.fused_keys:
+            idx_score_dense_keys(self.queries[0], self.kp, self.rows, self.S, self.keys,
+                                 skip_le_blocks=self.kb, ws=self.ws, stream=stream)
+        else:
+            idx_score_dense(self.queries[0], self.kp, self.rows, self.S, ws=self.ws, stream=stream)
         self._mark("dense>")
 
     def publish(self):
@@ -84,9 +92,11 @@ class Chunk:
         for t in (self.S, self.keys, *self.table.tensors(), self.rows.req, self.rows.len):
             t.record_stream(self.side)
         with torch.cuda.stream(self.side):
-            self._mark("amax8<")
-            idx_amax8_varlen(self.S, self.rows.len, self.keys, skip_le_blocks=self.kb)
-            self._mark("amax8>")
+            if not self.fused_keys:
+                self._mark("amax8<")
+                idx_amax8_varlen(self.S, self.rows.len, self.keys, skip_le_blocks=self.kb)
+                self._mark("amax8>")
+            self._mark("topk_blocks<")
             idx_topk_blocks(self.keys, self.rows.len, self.kb, self.table.blocks, self.table.n_kept)
             self._mark("topk_blocks>")
             idx_expand_candidates(self.kp, self.rows, self.table)   # records table.ready

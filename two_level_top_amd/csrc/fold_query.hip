@@ -38,59 +38,76 @@ __device__ __forceinline__ int e2m1_nearest(double a) {
   return 7;
 }
 
-// max over the 32 lanes of a half-wave
-__device__ __forceinline__ double halfwave_max(double v) {
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  return v;
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(v), CTRL, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xf, 0xf, true);
+  return __hiloint2double(hi, lo);
 }
 
-// One wave per query row; lane l owns dimensions l and l + 64 (groups l / 32
-// and 2 + l / 32).
+// 16 lanes per query row (4 rows per wave); lane j of a row owns dimensions
+// 8j .. 8j+7, i.e. one 4-byte word of every head's codes, and the 4 lanes of
+// an aligned quad together own one 32-element scale group.
+constexpr int kFoldRowsPerWG = 16;
+
 __global__ __launch_bounds__(256) void fold_query_kernel(QueryArgs q, uint8_t* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= q.rows) return;
-  double r[2] = {0.0, 0.0};
-  for (int h = 0; h < q.heads; ++h) {
-    const size_t base = (size_t)row * q.heads + h;
-    const double wh = 0.5 * (double)q.w[base];
+  const int row = blockIdx.x * kFoldRowsPerWG + (threadIdx.x >> 4);
+  const bool live = row < q.rows;
+  const int rr = live ? row : q.rows - 1;   // dead lanes compute a copy and store nothing
+  const int j = threadIdx.x & 15;
+  const int g = j >> 2;
+  const uint32_t* vrow = reinterpret_cast<const uint32_t*>(q.vals + (size_t)rr * q.heads * kValBytes) + j;
+  const uint8_t* srow = q.scales + (size_t)rr * q.heads * kScaleBytes + g;
+  const float* wrow = q.w + (size_t)rr * q.heads;
+  double r[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int d = lane + 64 * j;
-      const uint8_t byte = q.vals[base * kValBytes + d / 2];
-      const int code = (d & 1) ? (byte >> 4) : (byte & 15);
-      const int sc = q.scales[base * kScaleBytes + d / 32];
-      r[j] = fma(wh, ldexp(e2m1_value(code), sc - 127), r[j]);
+  for (int k = 0; k < 8; ++k) r[k] = 0.0;
+  // qf = sum_h (w_h / 2) q_h, exact products, fp64 sums in head order
+#pragma unroll 4
+  for (int h = 0; h < q.heads; ++h) {
+    const uint32_t v = vrow[h * (kValBytes / 4)];
+    // (w/2) * 2^(scale - 127), halved again because the codes below are 2|x|
+    const double ws = ldexp(0.5 * (double)wrow[h], (int)srow[h * kScaleBytes] - 128);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int code = (v >> (4 * k)) & 15;
+      const int m2 = (0xC8643210u >> (4 * (code & 7))) & 15;   // 2 * |e2m1 value|
+      r[k] = fma(ws, (double)((code & 8) ? -m2 : m2), r[k]);
     }
   }
   uint8_t* orow = out + (size_t)row * kFoldRowBytes;
   for (int t = 0; t < kFoldTerms; ++t) {
+    double m = 0.0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int d = lane + 64 * j;
-      const double m = halfwave_max(fabs(r[j]));
-      int e = -127;
-      if (m > 0.0) {
-        int x;
-        const double f = frexp(m / 6.0, &x);  // m / 6 = f * 2^x, f in [0.5, 1)
-        e = f > 0.5 ? x : x - 1;               // ceil(log2(m / 6))
-        e = e < -127 ? -127 : (e > 127 ? 127 : e);
-      }
-      const double a = ldexp(fabs(r[j]), -e);
-      int code = e2m1_nearest(a);
-      if (r[j] < 0.0 && code != 0) code |= 8;
-      r[j] -= ldexp(e2m1_value(code), e);
-      const int other = __shfl_xor(code, 1, 64);  // the neighbouring dimension
-      if ((d & 1) == 0) orow[t * kValBytes + d / 2] = (uint8_t)(code | (other << 4));
-      if ((d & 31) == 0) orow[kFoldTerms * kValBytes + t * kScaleBytes + d / 32] = (uint8_t)(e + 127);
+    for (int k = 0; k < 8; ++k) m = fmax(m, fabs(r[k]));
+    m = fmax(m, dpp_d<0xB1>(m));   // quad_perm [1,0,3,2]
+    m = fmax(m, dpp_d<0x4E>(m));   // quad_perm [2,3,0,1]: the group's max
+    int e = -127;
+    if (m > 0.0) {
+      int x;
+      const double f = frexp(m / 6.0, &x);  // m / 6 = f * 2^x, f in [0.5, 1)
+      e = f > 0.5 ? x : x - 1;               // ceil(log2(m / 6))
+      e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    }
+    uint32_t codes = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int code = e2m1_nearest(ldexp(fabs(r[k]), -e));
+      if (r[k] < 0.0 && code != 0) code |= 8;
+      r[k] -= ldexp(e2m1_value(code), e);
+      codes |= (uint32_t)code << (4 * k);
+    }
+    if (live) {
+      *reinterpret_cast<uint32_t*>(orow + t * kValBytes + 4 * j) = codes;
+      if ((j & 3) == 0) orow[kFoldTerms * kValBytes + t * kScaleBytes + g] = (uint8_t)(e + 127);
     }
   }
 }
 
 hipError_t launch_fold_query(const QueryArgs& q, uint8_t* out, hipStream_t st) {
   if (q.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fold_query_kernel, dim3((q.rows + 3) / 4), dim3(256), 0, st, q, out);
+  hipLaunchKernelGGL(fold_query_kernel, dim3((q.rows + kFoldRowsPerWG - 1) / kFoldRowsPerWG), dim3(256), 0,
+                     st, q, out);
   return hipGetLastError();
 }
 

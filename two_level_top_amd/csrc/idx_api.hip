@@ -42,6 +42,7 @@ idx_status check_query(const idx_query* q, const char* fn) {
   if (q->rows > 0 && (!q->vals || !q->scales || !q->w))
     return fail(IDX_E_ARG, "%s: query vals/scales/w is NULL", fn);
   if (!aligned(q->vals, 16)) return fail(IDX_E_ALIGN, "%s: query vals must be 16-byte aligned", fn);
+  if (!aligned(q->scales, 4)) return fail(IDX_E_ALIGN, "%s: query scales must be 4-byte aligned", fn);
   if (!aligned(q->w, 4)) return fail(IDX_E_ALIGN, "%s: query w must be 4-byte aligned", fn);
   return IDX_OK;
 }
@@ -125,24 +126,50 @@ size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k) {
   }
 }
 
-idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows, float* S,
-                           int64_t ld, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "idx_score_dense";
+// row offsets of S and of the keys are 32-bit byte offsets inside the kernels
+constexpr int64_t kMaxScoreLd = (int64_t)1 << 29;
+
+static idx_status score_dense_impl(const idx_query* q, const idx_kpool* kp, const idx_rows* rows,
+                                   float* S, int64_t ld, float* keys, int64_t ldk, int32_t skip,
+                                   void* ws, size_t ws_bytes, hipStream_t stream, const char* fn) {
   TRY(check_query(q, fn));
   TRY(check_pool(kp, fn, true));
   TRY(check_rows(rows, fn));
   if (q->rows != rows->rows) return fail(IDX_E_SHAPE, "%s: query rows %d != rows %d", fn, q->rows, rows->rows);
   if (ld < 1) return fail(IDX_E_ARG, "%s: ld < 1", fn);
+  if (ld > kMaxScoreLd) return fail(IDX_E_ARG, "%s: ld %lld above 2^29", fn, (long long)ld);
+  if (keys) {
+    if (skip < 0) return fail(IDX_E_ARG, "%s: skip_le_blocks < 0", fn);
+    if (ld % idxk::kBlock != 0)
+      return fail(IDX_E_ALIGN, "%s: ld %lld must be a multiple of 8 (whole blocks)", fn, (long long)ld);
+    if (ldk < 1) return fail(IDX_E_ARG, "%s: ldk must hold at least one key per row", fn);
+  }
   if (rows->rows == 0) return ok();
   if (!S) return fail(IDX_E_ARG, "%s: S is NULL", fn);
   if (!aligned(S, 4)) return fail(IDX_E_ALIGN, "%s: S must be 4-byte aligned", fn);
+  if (keys && !aligned(keys, 4)) return fail(IDX_E_ALIGN, "%s: keys must be 4-byte aligned", fn);
   TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
   idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
   idxk::PoolArgs pa{kp->pool, kp->num_pages, kp->page_table, kp->num_req, kp->max_pages};
   uint8_t* fold = static_cast<uint8_t*>(ws);
   hipError_t e = idxk::launch_fold_query(qa, fold, stream);
   if (e != hipSuccess) return hip_status(e, fn);
-  return hip_status(idxk::launch_score_dense(qa, fold, pa, rows->req, rows->len, S, ld, stream), fn);
+  return hip_status(idxk::launch_score_dense(qa, fold, pa, rows->req, rows->len, S, ld, keys, ldk,
+                                             skip, stream), fn);
+}
+
+idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows, float* S,
+                           int64_t ld, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return score_dense_impl(q, kp, rows, S, ld, nullptr, 0, 0, ws, ws_bytes, stream, "idx_score_dense");
+}
+
+idx_status idx_score_dense_keys(const idx_query* q, const idx_kpool* kp, const idx_rows* rows,
+                                float* S, int64_t ld, float* keys, int64_t ldk,
+                                int32_t skip_le_blocks, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  const char* fn = "idx_score_dense_keys";
+  if (!keys && rows && rows->rows > 0) return fail(IDX_E_ARG, "%s: keys is NULL", fn);
+  return score_dense_impl(q, kp, rows, S, ld, keys, ldk, skip_le_blocks, ws, ws_bytes, stream, fn);
 }
 
 idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int32_t rows,

@@ -45,9 +45,11 @@ __device__ __forceinline__ int clamp_req(int r, int num_req) {
 // writes kFoldRowBytes per query row (see fold_query.hip)
 hipError_t launch_fold_query(const QueryArgs& q, uint8_t* out, hipStream_t st);
 
+// keys == nullptr: scores only; otherwise also the block keys of
+// idx_amax8_varlen(S, ld, len, rows, keys, ldk, skip).
 hipError_t launch_score_dense(const QueryArgs& q, const uint8_t* fold, const PoolArgs& kp,
                               const int32_t* req, const int32_t* len, float* S, int64_t ld,
-                              hipStream_t st);
+                              float* keys, int64_t ldk, int skip, hipStream_t st);
 
 hipError_t launch_amax8(const float* S, int64_t ld, const int32_t* len, int rows, float* keys,
                         int64_t ldk, int skip, hipStream_t st);
@@ -133,6 +135,18 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Raw buffer resource over [p, p + bytes): accesses past the end are dropped
+// (stores) or read as zero (loads) by the hardware, so ragged edges need no
+// branches.  Dword 3 = 32-bit data format, the raw-buffer setting of gfx9.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 __device__ __forceinline__ int64_t clamp_page(int64_t page, int num_pages) {

@@ -14,9 +14,25 @@
 //   the folded query block) in registers and streams K one pool page (64
 //   positions, 4 MFMA tiles) at a time straight from the paged pool: lane l
 //   loads 16 bytes of position (l % 16) of each tile, so a page's 4 KB of
-//   codes is read with 4 fully coalesced loads per wave.
+//   codes is read with 4 fully coalesced loads per wave.  Two pages are in
+//   flight (ping-pong registers, no copies); pages are read through a buffer
+//   resource and scores/keys stored through resources sized to the row's
+//   valid range, so the loop has no branches (out-of-range lanes are dropped
+//   by the hardware).
 // Rows of a wave that belong to different requests are scored one after
 // the other (their keys come from different pages).
+//
+// Measured on MI355X (long chunk): this 16x16x128 form at 3 waves per SIMD
+// beat a 32x32x64 form of the same epilogue (2 waves per SIMD at 249 VGPRs)
+// by about 12%, and issuing the next tile's MFMAs ahead of the epilogue or
+// deferring the stores past the next loads gained nothing.
+//
+// Fused block keys (the prefill PR's follow-up of folding the block amax into
+// the score kernel): after the 4-way reduction each lane holds one score of
+// 64 consecutive positions, so an aligned 8-lane DPP max gives the key of
+// every block of the page without reading S back.  The keys equal what
+// idx_amax8_varlen computes from the stored S (the max of the same fp32
+// values; the newest block is +inf; rows with nblk <= skip are untouched).
 #include "score_common.h"
 
 namespace idxk {
@@ -27,44 +43,68 @@ constexpr int kDenseRowsPerWave = 2;
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Where the fused block keys go (keys == nullptr: not requested).
+struct KeyArgs {
+  float* keys;
+  int64_t ldk;
+  int skip;
+};
+
+// max over the aligned group of 8 lanes, in every lane of the group: three
+// DPP maxes (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror); the s_nop
+// covers the VALU-write -> DPP-read hazard.  Written out because the compiler
+// would canonicalize both operands of every fmaxf.
+__device__ __forceinline__ float max8_lanes(float v) {
+  float a, b, c;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=v"(a) : "v"(v));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=v"(b) : "v"(a));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=v"(c) : "v"(b));
+  return c;
+}
+
 // K operands of one pool page: 4 MFMA tiles of 16 positions.
 struct PageOps {
   uint4 b[4];
   int sb[4];
 };
 
-__device__ __forceinline__ void load_page(const uint8_t* pg, int voff, int soff, PageOps& o) {
+__device__ __forceinline__ void load_page(__amdgpu_buffer_rsrc_t pg, uint32_t voff, uint32_t soff, PageOps& o) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    o.b[t] = *reinterpret_cast<const uint4*>(pg + voff + t * 16 * kValBytes);
-    o.sb[t] = pg[soff + t * 16 * kScaleBytes];
+    o.b[t] = buffer_load_b128(pg, voff + t * 16 * kValBytes);
+    o.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(pg, soff + t * 16 * kScaleBytes, 0, 0);
   }
 }
 
 // Score NR (1 or 2) rows of one request against positions [c0, cend) (c0 on
 // a page boundary, at most 16 pages).  Every tile of a page is computed;
-// positions past a row's length are never stored.
-//
-// Software pipeline: the MFMAs of tile i+1 are issued before the epilogue
-// FMAs of tile i, so the matrix core and the VALU work at the same time
-// within one wave (the epilogue costs about as many cycles as the MFMAs).
-template <int HB, int NR>
+// positions past a row's length are never stored.  With KEYS, Krow[r] gets
+// the keys of blocks [c0/8, min(cend/8, nblk[r])) (Krow[r] is only used when
+// nblk[r] > 0, i.e. the row is keyed).
+template <int HB, int NR, bool KEYS>
 __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* const (&Srow)[2],
-                                           const int (&lens)[2], const uint8_t* pool,
+                                           const int (&lens)[2], float* const (&Krow)[2],
+                                           const int (&nblk)[2], const uint8_t* pool,
                                            int num_pages, const int32_t* pt, int max_pages,
                                            int c0, int cend, int lane) {
-  const int voff = (lane & 15) * kValBytes + (lane >> 4) * 16;
-  const int soff = kPageValBytes + (lane & 15) * kScaleBytes + (lane >> 4);
-  // the chunk's page ids, one per lane, read back with readlane
+  const uint32_t voff = (uint32_t)((lane & 15) * kValBytes + (lane >> 4) * 16);
+  const uint32_t soff = (uint32_t)(kPageValBytes + (lane & 15) * kScaleBytes + (lane >> 4));
   const int npg = (cend - c0 + kPage - 1) / kPage;
   const int pid = (int)clamp_page(pt[min(c0 / kPage + min(lane, npg - 1), max_pages - 1)], num_pages);
-  auto page_ptr = [&](int i) {
-    return pool + (int64_t)__builtin_amdgcn_readlane(pid, i) * kPageBytes;
+  auto load = [&](int i, PageOps& o) {
+    const int64_t pg = __builtin_amdgcn_readlane(pid, min(i, npg - 1));
+    load_page(buffer_rsrc(pool + pg * kPageBytes, kPageBytes), voff, soff, o);
   };
-  PageOps cur, nxt;
-  load_page(page_ptr(0), voff, soff, cur);
-  for (int i = 0; i < npg; ++i) {
-    load_page(page_ptr(min(i + 1, npg - 1)), voff, soff, nxt);
+  __amdgpu_buffer_rsrc_t rs[2], rk[2];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    rs[r] = buffer_rsrc(Srow[r], (uint32_t)lens[r] * 4u);
+    if (KEYS) rk[r] = buffer_rsrc(Krow[r], (uint32_t)nblk[r] * 4u);
+  }
+  auto compute = [&](int i, const PageOps& cur) {
     float part[NR][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -78,19 +118,34 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* con
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const float tot = reduce_scatter4(part[r][0], part[r][1], part[r][2], part[r][3]);
-      if (p < lens[r]) Srow[r][p] = tot;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rs[r], (uint32_t)p * 4u, 0, 0);
+      if (KEYS) {
+        const float m = max8_lanes(tot);
+        const int blk = p >> 3;
+        const float key = blk == nblk[r] - 1 ? __builtin_inff() : m;
+        const uint32_t koff = (lane & 7) == 0 ? (uint32_t)blk * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key), rk[r], koff, 0, 0);
+      }
     }
-    cur = nxt;
+  };
+  PageOps A, B;
+  load(0, A);
+  for (int i = 0; i < npg; i += 2) {
+    load(i + 1, B);
+    compute(i, A);
+    if (i + 1 >= npg) break;
+    load(i + 2, A);
+    compute(i + 1, B);
   }
 }
 
-template <int HB>
-__global__ __launch_bounds__(256) void score_dense_kernel(QueryArgs q, const uint8_t* __restrict__ fold,
+template <int HB, bool KEYS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void score_dense_kernel(QueryArgs q, const uint8_t* __restrict__ fold,
                                                           PoolArgs kp,
                                                           const int32_t* __restrict__ req,
                                                           const int32_t* __restrict__ len,
                                                           float* __restrict__ S, int64_t ld,
-                                                          int nchunks) {
+                                                          KeyArgs ka, int nchunks) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int chunk = blockIdx.x % nchunks;
@@ -106,6 +161,19 @@ __global__ __launch_bounds__(256) void score_dense_kernel(QueryArgs q, const uin
   const int len0 = uniform(min(max(len[r0], 0), lcap));
   const int req1 = r1 >= 0 ? uniform(clamp_req(req[r1], kp.num_req)) : -1;
   const int len1 = r1 >= 0 ? uniform(min(max(len[r1], 0), lcap)) : 0;
+  // keyed rows: nblk > skip, capped like idx_amax8_varlen (ldk and ld / 8);
+  // nblk = 0 marks a row without keys
+  int nblk[2] = {0, 0};
+  float* Krow[2] = {nullptr, nullptr};
+  if (KEYS) {
+    const int64_t kcap = min(ka.ldk, ld / kBlock);
+    const int nb0 = (int)min((int64_t)((len0 + kBlock - 1) / kBlock), kcap);
+    const int nb1 = (int)min((int64_t)((len1 + kBlock - 1) / kBlock), kcap);
+    nblk[0] = nb0 > ka.skip ? nb0 : 0;
+    nblk[1] = nb1 > ka.skip ? nb1 : 0;
+    Krow[0] = ka.keys + (int64_t)r0 * ka.ldk;
+    Krow[1] = r1 >= 0 ? ka.keys + (int64_t)r1 * ka.ldk : Krow[0];
+  }
   const int c0 = chunk * kDenseChunk;
   RowFrag<HB> f[2];
   float* Srow[2];
@@ -119,8 +187,8 @@ __global__ __launch_bounds__(256) void score_dense_kernel(QueryArgs q, const uin
     Srow[1] = S + (int64_t)r1 * ld;
     lens[0] = len0;
     lens[1] = len1;
-    score_rows<HB, 2>(f, Srow, lens, kp.pool, kp.num_pages, kp.page_table + (int64_t)req0 * kp.max_pages,
-                      kp.max_pages, c0, cend, lane);
+    score_rows<HB, 2, KEYS>(f, Srow, lens, Krow, nblk, kp.pool, kp.num_pages,
+                            kp.page_table + (int64_t)req0 * kp.max_pages, kp.max_pages, c0, cend, lane);
     return;
   }
   for (int i = 0; i < 2; ++i) {  // rows of different requests, one at a time
@@ -135,14 +203,28 @@ __global__ __launch_bounds__(256) void score_dense_kernel(QueryArgs q, const uin
     Srow[1] = Srow[0];
     lens[0] = L;
     lens[1] = 0;
-    score_rows<HB, 1>(f, Srow, lens, kp.pool, kp.num_pages, kp.page_table + (int64_t)rq * kp.max_pages,
-                      kp.max_pages, c0, cend, lane);
+    float* const Kr[2] = {Krow[i], Krow[i]};
+    const int nb[2] = {nblk[i], 0};
+    score_rows<HB, 1, KEYS>(f, Srow, lens, Kr, nb, kp.pool, kp.num_pages,
+                            kp.page_table + (int64_t)rq * kp.max_pages, kp.max_pages, c0, cend, lane);
+  }
+}
+
+template <bool KEYS>
+static void launch_dense_hb(int hb, dim3 grid, hipStream_t st, const QueryArgs& q, const uint8_t* fold,
+                            const PoolArgs& kp, const int32_t* req, const int32_t* len, float* S,
+                            int64_t ld, const KeyArgs& ka, int nchunks) {
+  switch (hb) {
+    case 1: hipLaunchKernelGGL((score_dense_kernel<1, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
+    case 2: hipLaunchKernelGGL((score_dense_kernel<2, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
+    case 3: hipLaunchKernelGGL((score_dense_kernel<3, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
+    default: hipLaunchKernelGGL((score_dense_kernel<4, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
   }
 }
 
 hipError_t launch_score_dense(const QueryArgs& q, const uint8_t* fold, const PoolArgs& kp,
                               const int32_t* req, const int32_t* len, float* S, int64_t ld,
-                              hipStream_t st) {
+                              float* keys, int64_t ldk, int skip, hipStream_t st) {
   const int rows_per_wg = kDenseWaves * kDenseRowsPerWave;
   const int64_t groups = (q.rows + rows_per_wg - 1) / rows_per_wg;
   const int nchunks = (int)((ld + kDenseChunk - 1) / kDenseChunk);
@@ -150,12 +232,11 @@ hipError_t launch_score_dense(const QueryArgs& q, const uint8_t* fold, const Poo
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int hb = (q.heads + 15) / 16;
-  switch (hb) {
-    case 1: hipLaunchKernelGGL(score_dense_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, kp, req, len, S, ld, nchunks); break;
-    case 2: hipLaunchKernelGGL(score_dense_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, kp, req, len, S, ld, nchunks); break;
-    case 3: hipLaunchKernelGGL(score_dense_kernel<3>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, kp, req, len, S, ld, nchunks); break;
-    default: hipLaunchKernelGGL(score_dense_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, kp, req, len, S, ld, nchunks); break;
-  }
+  const KeyArgs ka{keys, ldk, skip};
+  if (keys)
+    launch_dense_hb<true>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks);
+  else
+    launch_dense_hb<false>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks);
   return hipGetLastError();
 }
 
