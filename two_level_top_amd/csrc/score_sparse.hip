@@ -5,17 +5,23 @@
 // order; no dense row is formed).
 //
 // The work list (built by idx_expand_candidates) holds one unit per 64
-// candidate blocks of a row.  A wave takes a unit, keeps the row's query in
-// registers, loads the unit's 64 pool-block ids once (one per lane) and walks
-// 2 candidate blocks (16 positions) per MFMA tile, 4 tiles per group with the
-// next group's K prefetched: lane l gathers 16 bytes of position (l % 8) of
-// block (l % 16) / 8 -- each block is 512 contiguous value bytes and 32
-// contiguous scale bytes of one pool page.
+// candidate blocks of a row.  A wave takes 8 consecutive units (the list is
+// row-major, so mostly of one row), keeps the row's query in registers across
+// them, loads each unit's 64 pool-block ids once (one per lane) and walks
+// 2 candidate blocks (16 positions) per MFMA tile, 4 tiles per group, two
+// groups in flight (ping-pong registers): lane l gathers 16 bytes of position
+// (l % 8) of block (l % 16) / 8 -- each block is 512 contiguous value bytes
+// and 32 contiguous scale bytes of one pool page.  Loads go through one
+// buffer resource over the pool and scores are stored through a resource
+// sized to the unit's valid columns, so the loop has no branches.
 #include "score_common.h"
 
 namespace idxk {
 
 constexpr int kSparseWaves = 4;
+// units per wave; 8 and 32 measured alike on MI355X, 1 was 8% slower (the
+// query reload and the wave launch per 512 columns)
+constexpr int kUnitsPerWave = 8;
 
 // K operands of 4 tiles (8 candidate blocks) of one unit.
 struct GroupOps {
@@ -23,27 +29,22 @@ struct GroupOps {
   int sb[4];
 };
 
-// Lane l needs position (l % 8) of block 2 t + (l % 16) / 8 of the group;
-// the blocks' pool ids come from the unit's id vector `pbv` (lane i holds
-// candidate block first + i) by readlane, so no per-tile address load is
-// on the critical path.  Blocks past `nblk` (the unit's end) read block 0 of
-// the unit and are never stored.
-// `bov` holds, in lane i, the byte offset of candidate block first + i's
-// values in the pool (its scales sit at bov + 4096 - 7 * 64 * (block in page),
-// folded into `sov`).
-__device__ __forceinline__ void load_group(const uint8_t* pool, uint32_t bov, uint32_t sov, int g,
-                                           int nblk, int lane, GroupOps& o) {
-  const int slot = lane & 7;
-  const bool half = (lane >> 3) & 1;
-  const uint32_t voff = slot * kValBytes + (lane >> 4) * 16;
-  const uint32_t soff = slot * kScaleBytes + (lane >> 4);
+// Lane l of tile t of group g needs position (l % 8) of candidate block
+// 8 g + 2 t + (l / 8) % 2, 16 bytes at (l / 16) * 16 of its values and byte
+// l / 16 of its scales.  The unit's block byte offsets sit one per lane in
+// `bov` (values) and `sov` (scales); ds_bpermute hands each lane its block's
+// pair (the tile's block index is the instruction's immediate offset), so
+// addressing costs one add per operand.  Blocks past the unit's end repeat
+// its last block and are never stored.
+__device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t pool, int bov, int sov, int sel,
+                                           uint32_t voff, uint32_t soff, GroupOps& o) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int i0 = min(8 * g + 2 * t, nblk - 1), i1 = min(8 * g + 2 * t + 1, nblk - 1);
-    const uint32_t v0 = __builtin_amdgcn_readlane(bov, i0), v1 = __builtin_amdgcn_readlane(bov, i1);
-    const uint32_t s0 = __builtin_amdgcn_readlane(sov, i0), s1 = __builtin_amdgcn_readlane(sov, i1);
-    o.b[t] = *reinterpret_cast<const uint4*>(pool + (half ? v1 : v0) + voff);
-    o.sb[t] = pool[(half ? s1 : s0) + soff];
+    const int a = sel + 8 * t;   // byte address of the source lane (block 8g + 2t + half)
+    const uint32_t vb = (uint32_t)__builtin_amdgcn_ds_bpermute(a, bov);
+    const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(a, sov);
+    o.b[t] = buffer_load_b128(pool, vb + voff);
+    o.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(pool, sb + soff, 0, 0);
   }
 }
 
@@ -61,7 +62,17 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int max_units = q.rows * ((kb + kUnitBlocks - 1) / kUnitBlocks);
   const int nunits = min(sched[0], max_units);
-  for (int u = blockIdx.x * kSparseWaves + wave; u < nunits; u += gridDim.x * kSparseWaves) {
+  const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(pool, (uint32_t)num_pages * (uint32_t)kPageBytes);
+  const uint32_t voff = (uint32_t)((lane & 7) * kValBytes + (lane >> 4) * 16);
+  const uint32_t soff = (uint32_t)((lane & 7) * kScaleBytes + (lane >> 4));
+  const int half = (lane >> 3) & 1;
+  // each wave takes kUnitsPerWave consecutive units (mostly of one row: the
+  // list is row-major) and keeps the row's query in registers across them
+  const int u0 = (blockIdx.x * kSparseWaves + wave) * kUnitsPerWave;
+  const int u1 = min(u0 + kUnitsPerWave, nunits);
+  int cur_row = -1;
+  RowFrag<HB> f;
+  for (int u = u0; u < u1; ++u) {
     const int row = __builtin_amdgcn_readfirstlane(sched[4 + 2 * u]);
     const int first = __builtin_amdgcn_readfirstlane(sched[5 + 2 * u]);
     if (row < 0 || row >= q.rows || first < 0) continue;   // not a work list this table built
@@ -69,19 +80,21 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
     const int vl = __builtin_amdgcn_readfirstlane(min(valid_len[row], nk * kBlock));
     const int nblk = min(kUnitBlocks, nk - first);   // candidate blocks of this unit
     if (nblk <= 0) continue;
-    RowFrag<HB> f;
-    load_row(q, fold, row, lane, f);
+    if (row != cur_row) {
+      load_row(q, fold, row, lane, f);
+      cur_row = row;
+    }
     // byte offsets of this lane's candidate block (pools are < 4 GiB here)
     const int pb = phys[(int64_t)row * kb + first + min(lane, nblk - 1)];
     const uint32_t pgo = (uint32_t)clamp_page(pb >> 3, num_pages) * (uint32_t)kPageBytes;
-    const uint32_t bov = pgo + (uint32_t)(pb & 7) * (kBlock * kValBytes);
-    const uint32_t sov = pgo + kPageValBytes + (uint32_t)(pb & 7) * (kBlock * kScaleBytes);
-    float* Tr = T + (int64_t)row * ld + first * kBlock;
+    const int bov = (int)(pgo + (uint32_t)(pb & 7) * (kBlock * kValBytes));
+    const int sov = (int)(pgo + kPageValBytes + (uint32_t)(pb & 7) * (kBlock * kScaleBytes));
+    // valid columns of this unit: stores past them are dropped by the resource
+    const int ncols = max(0, min(vl - first * kBlock, nblk * kBlock));
+    const __amdgpu_buffer_rsrc_t trs = buffer_rsrc(T + (int64_t)row * ld + first * kBlock, (uint32_t)ncols * 4u);
     const int ngroups = (nblk + 7) / 8;
-    GroupOps cur, nxt;
-    load_group(pool, bov, sov, 0, nblk, lane, cur);
-    for (int g = 0; g < ngroups; ++g) {
-      load_group(pool, bov, sov, min(g + 1, ngroups - 1), nblk, lane, nxt);
+    auto sel_of = [&](int g) { return 4 * min(8 * g + half, nblk - 1); };
+    auto compute = [&](int g, const GroupOps& cur) {
       float p[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -90,9 +103,16 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
         p[t] = tile_epilogue<HB>(f, acc);
       }
       const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
-      const int c = g * 64 + lane;   // column within the unit
-      if (first * kBlock + c < vl && c < nblk * kBlock) Tr[c] = tot;
-      cur = nxt;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), trs, (uint32_t)(g * 64 + lane) * 4u, 0, 0);
+    };
+    GroupOps A, B;
+    load_group(prs, bov, sov, sel_of(0), voff, soff, A);
+    for (int g = 0; g < ngroups; g += 2) {
+      load_group(prs, bov, sov, sel_of(min(g + 1, ngroups - 1)), voff, soff, B);
+      compute(g, A);
+      if (g + 1 >= ngroups) break;
+      load_group(prs, bov, sov, sel_of(min(g + 2, ngroups - 1)), voff, soff, A);
+      compute(g + 1, B);
     }
   }
 }
@@ -103,9 +123,10 @@ hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const ui
                                const int32_t* valid_len, int rows, int kb, const void* schedule,
                                float* T, int64_t ld, hipStream_t st) {
   const int64_t max_units = (int64_t)rows * ((kb + kUnitBlocks - 1) / kUnitBlocks);
-  int64_t grid = (max_units + kSparseWaves - 1) / kSparseWaves;
+  const int64_t per_wg = (int64_t)kSparseWaves * kUnitsPerWave;
+  int64_t grid = (max_units + per_wg - 1) / per_wg;
   if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL) grid = 0x7fffffffLL;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int32_t* sched = static_cast<const int32_t*>(schedule);
   const int hb = (q.heads + 15) / 16;
   switch (hb) {

@@ -74,20 +74,49 @@ struct TopkShared {
   uint32_t bcast[4];
 };
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// Wave-wide reductions and scans on DPP and permlane moves (VALU only; the
+// shuffle forms go through LDS with a round trip per step).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, true);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_shr(uint32_t v) {   // row_shr: lanes shifted in read 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, true);
+}
+// combine each lane with lanes l ^ 32 and then l ^ 16 (rows already reduced)
+template <class Op>
+__device__ __forceinline__ uint32_t rows_reduce(uint32_t v, Op op) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return op(b[0], b[1]);
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+  v = op(v, dpp_u<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_u<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_u<0x141>(v));   // row_half_mirror: the 8-lane halves
+  v = op(v, dpp_u<0x140>(v));   // row_mirror: the 16-lane row
+  return rows_reduce(v, op);
 }
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_shr<0x111>(x);   // row_shr:1
+  x += dpp_shr<0x112>(x);   // row_shr:2
+  x += dpp_shr<0x114>(x);   // row_shr:4
+  x += dpp_shr<0x118>(x);   // row_shr:8
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t t1 = t0 + (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t t2 = t1 + (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row == 0 ? 0u : (row == 1 ? t0 : (row == 2 ? t1 : t2)));
 }
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -144,12 +173,7 @@ __device__ __forceinline__ int find_bin(TopkShared& sh, uint32_t rem, uint32_t* 
     cb[q] = sh.hist[kBins - 1 - BPT * tid - q];
     csum += cb[q];
   }
-  uint32_t x = csum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(csum);
   if (lane == 63) sh.wcnt[wave][0] = x;
   __syncthreads();
   uint32_t before = 0u;
@@ -305,17 +329,12 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
       for (int j = 0; j < kTopkSteps; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) mine += digit0c(key[j][e]) == bin ? 1u : 0u;
-      uint32_t x = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
-      const uint32_t wtot = __shfl(x, 63, 64);
+      const uint32_t x = wave_incl_scan(mine);
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
       if (wtot != 0u) {
         uint32_t base = 0u;
         if (lane == 0) base = atomicAdd(&sh.bcast[2], wtot);
-        base = __shfl(base, 0, 64);
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
         uint32_t pre = base + x - mine;
 #pragma unroll
         for (int j = 0; j < kTopkSteps; ++j)
