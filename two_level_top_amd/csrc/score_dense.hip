@@ -5,7 +5,8 @@
 // each row's [ks, ke)).
 //
 // Work decomposition (gfx950: 256 CUs in 8 XCDs, wave64):
-//   workgroup = 4 waves, 8 query rows (2 per wave), 1024 positions.
+//   workgroup = 4 waves, 8 query rows (2 per wave), 1024 positions (512 or
+//   256 when there are too few rows to fill the chip otherwise, as in decode).
 //   workgroup id -> (row group = id / nchunks, chunk = id % nchunks), so
 //   consecutive ids -- which the dispatcher spreads over the 8 XCDs -- share
 //   a row group and walk different position chunks: each XCD keeps 1/8 of
@@ -37,7 +38,11 @@
 
 namespace idxk {
 
-constexpr int kDenseChunk = 1024;
+// positions per workgroup: 1024, or 512 / 256 when there are few rows (decode)
+// so that at least kDenseTargetWGs workgroups run
+constexpr int kDenseMaxChunk = 1024;
+constexpr int kDenseMinChunk = 256;
+constexpr int64_t kDenseTargetWGs = 2048;
 constexpr int kDenseWaves = 4;
 constexpr int kDenseRowsPerWave = 2;
 
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
                                                           const int32_t* __restrict__ req,
                                                           const int32_t* __restrict__ len,
                                                           float* __restrict__ S, int64_t ld,
-                                                          KeyArgs ka, int nchunks) {
+                                                          KeyArgs ka, int nchunks, int chunk_len) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int chunk = blockIdx.x % nchunks;
@@ -174,12 +179,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     Krow[0] = ka.keys + (int64_t)r0 * ka.ldk;
     Krow[1] = r1 >= 0 ? ka.keys + (int64_t)r1 * ka.ldk : Krow[0];
   }
-  const int c0 = chunk * kDenseChunk;
+  const int c0 = chunk * chunk_len;
   RowFrag<HB> f[2];
   float* Srow[2];
   int lens[2];
   if (r1 >= 0 && req1 == req0) {  // both rows read the same keys
-    const int cend = min(c0 + kDenseChunk, max(len0, len1));
+    const int cend = min(c0 + chunk_len, max(len0, len1));
     if (c0 >= cend) return;
     load_row(q, fold, r0, lane, f[0]);
     load_row(q, fold, r1, lane, f[1]);
@@ -196,7 +201,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     if (r < 0) break;
     const int L = i == 0 ? len0 : len1;
     const int rq = i == 0 ? req0 : req1;
-    const int cend = min(c0 + kDenseChunk, L);
+    const int cend = min(c0 + chunk_len, L);
     if (c0 >= cend) continue;
     load_row(q, fold, r, lane, f[0]);
     Srow[0] = S + (int64_t)r * ld;
@@ -213,12 +218,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
 template <bool KEYS>
 static void launch_dense_hb(int hb, dim3 grid, hipStream_t st, const QueryArgs& q, const uint8_t* fold,
                             const PoolArgs& kp, const int32_t* req, const int32_t* len, float* S,
-                            int64_t ld, const KeyArgs& ka, int nchunks) {
+                            int64_t ld, const KeyArgs& ka, int nchunks, int chunk_len) {
   switch (hb) {
-    case 1: hipLaunchKernelGGL((score_dense_kernel<1, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
-    case 2: hipLaunchKernelGGL((score_dense_kernel<2, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
-    case 3: hipLaunchKernelGGL((score_dense_kernel<3, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
-    default: hipLaunchKernelGGL((score_dense_kernel<4, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks); break;
+    case 1: hipLaunchKernelGGL((score_dense_kernel<1, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
+    case 2: hipLaunchKernelGGL((score_dense_kernel<2, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
+    case 3: hipLaunchKernelGGL((score_dense_kernel<3, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
+    default: hipLaunchKernelGGL((score_dense_kernel<4, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
   }
 }
 
@@ -227,16 +232,19 @@ hipError_t launch_score_dense(const QueryArgs& q, const uint8_t* fold, const Poo
                               float* keys, int64_t ldk, int skip, hipStream_t st) {
   const int rows_per_wg = kDenseWaves * kDenseRowsPerWave;
   const int64_t groups = (q.rows + rows_per_wg - 1) / rows_per_wg;
-  const int nchunks = (int)((ld + kDenseChunk - 1) / kDenseChunk);
+  int chunk_len = kDenseMaxChunk;
+  while (chunk_len > kDenseMinChunk && groups * ((ld + chunk_len - 1) / chunk_len) < kDenseTargetWGs)
+    chunk_len /= 2;
+  const int nchunks = (int)((ld + chunk_len - 1) / chunk_len);
   const int64_t grid = groups * nchunks;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int hb = (q.heads + 15) / 16;
   const KeyArgs ka{keys, ldk, skip};
   if (keys)
-    launch_dense_hb<true>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks);
+    launch_dense_hb<true>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len);
   else
-    launch_dense_hb<false>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks);
+    launch_dense_hb<false>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len);
   return hipGetLastError();
 }
 

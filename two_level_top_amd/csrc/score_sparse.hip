@@ -19,9 +19,13 @@
 namespace idxk {
 
 constexpr int kSparseWaves = 4;
-// units per wave; 8 and 32 measured alike on MI355X, 1 was 8% slower (the
-// query reload and the wave launch per 512 columns)
-constexpr int kUnitsPerWave = 8;
+// Work per wave, chosen at launch from the number of units so that about
+// kSparseTargetWaves waves run: up to 8 consecutive units per wave on big
+// tables (8 and 32 measured alike on MI355X, 1 was 8% slower: the query
+// reload and the wave launch per 512 columns), or a unit split over 2, 4 or
+// 8 waves (8 / split groups each) when there are few rows, as in decode.
+constexpr int kSparseTargetWaves = 8192;
+constexpr int kMaxUnitsPerWave = 8;
 
 // K operands of 4 tiles (8 candidate blocks) of one unit.
 struct GroupOps {
@@ -57,7 +61,8 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
                                                            const int32_t* __restrict__ n_kept,
                                                            const int32_t* __restrict__ valid_len,
                                                            int kb, const int32_t* __restrict__ sched,
-                                                           float* __restrict__ T, int64_t ld) {
+                                                           float* __restrict__ T, int64_t ld,
+                                                           int upw, int split) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int max_units = q.rows * ((kb + kUnitBlocks - 1) / kUnitBlocks);
@@ -66,10 +71,14 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
   const uint32_t voff = (uint32_t)((lane & 7) * kValBytes + (lane >> 4) * 16);
   const uint32_t soff = (uint32_t)((lane & 7) * kScaleBytes + (lane >> 4));
   const int half = (lane >> 3) & 1;
-  // each wave takes kUnitsPerWave consecutive units (mostly of one row: the
-  // list is row-major) and keeps the row's query in registers across them
-  const int u0 = (blockIdx.x * kSparseWaves + wave) * kUnitsPerWave;
-  const int u1 = min(u0 + kUnitsPerWave, nunits);
+  // each wave takes `upw` consecutive units (mostly of one row: the list is
+  // row-major) and keeps the row's query in registers across them, or part
+  // `part` of one unit when split > 1
+  const int wid = blockIdx.x * kSparseWaves + wave;
+  const int u0 = split > 1 ? wid / split : wid * upw;
+  const int u1 = min(split > 1 ? u0 + 1 : u0 + upw, nunits);
+  const int part = split > 1 ? wid % split : 0;
+  const int gper = 8 / split;                      // groups per part
   int cur_row = -1;
   RowFrag<HB> f;
   for (int u = u0; u < u1; ++u) {
@@ -105,13 +114,16 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
       const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), trs, (uint32_t)(g * 64 + lane) * 4u, 0, 0);
     };
+    const int g0 = part * gper;
+    const int g1 = min(ngroups, g0 + gper);
+    if (g0 >= g1) continue;
     GroupOps A, B;
-    load_group(prs, bov, sov, sel_of(0), voff, soff, A);
-    for (int g = 0; g < ngroups; g += 2) {
-      load_group(prs, bov, sov, sel_of(min(g + 1, ngroups - 1)), voff, soff, B);
+    load_group(prs, bov, sov, sel_of(g0), voff, soff, A);
+    for (int g = g0; g < g1; g += 2) {
+      load_group(prs, bov, sov, sel_of(min(g + 1, g1 - 1)), voff, soff, B);
       compute(g, A);
-      if (g + 1 >= ngroups) break;
-      load_group(prs, bov, sov, sel_of(min(g + 2, ngroups - 1)), voff, soff, A);
+      if (g + 1 >= g1) break;
+      load_group(prs, bov, sov, sel_of(min(g + 2, g1 - 1)), voff, soff, A);
       compute(g + 1, B);
     }
   }
@@ -123,17 +135,24 @@ hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const ui
                                const int32_t* valid_len, int rows, int kb, const void* schedule,
                                float* T, int64_t ld, hipStream_t st) {
   const int64_t max_units = (int64_t)rows * ((kb + kUnitBlocks - 1) / kUnitBlocks);
-  const int64_t per_wg = (int64_t)kSparseWaves * kUnitsPerWave;
-  int64_t grid = (max_units + per_wg - 1) / per_wg;
-  if (grid <= 0) return hipSuccess;
+  if (max_units <= 0) return hipSuccess;
+  int upw = 1, split = 1;
+  if (max_units >= (int64_t)kSparseTargetWaves * kMaxUnitsPerWave)
+    upw = kMaxUnitsPerWave;
+  else if (max_units >= kSparseTargetWaves)
+    upw = (int)(max_units / kSparseTargetWaves);
+  else
+    while (split < 8 && max_units * split < kSparseTargetWaves) split *= 2;
+  const int64_t waves = split > 1 ? max_units * split : (max_units + upw - 1) / upw;
+  int64_t grid = (waves + kSparseWaves - 1) / kSparseWaves;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int32_t* sched = static_cast<const int32_t*>(schedule);
   const int hb = (q.heads + 15) / 16;
   switch (hb) {
-    case 1: hipLaunchKernelGGL(score_sparse_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
-    case 2: hipLaunchKernelGGL(score_sparse_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
-    case 3: hipLaunchKernelGGL(score_sparse_kernel<3>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
-    default: hipLaunchKernelGGL(score_sparse_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld); break;
+    case 1: hipLaunchKernelGGL(score_sparse_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
+    case 2: hipLaunchKernelGGL(score_sparse_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
+    case 3: hipLaunchKernelGGL(score_sparse_kernel<3>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
+    default: hipLaunchKernelGGL(score_sparse_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
   }
   return hipGetLastError();
 }
