@@ -320,3 +320,48 @@ def random_lengths(seed: int, rows: int, lo: int, hi: int, extra=()) -> np.ndarr
     for i, v in enumerate(extra[:rows]):
         out[i] = v
     return out
+
+
+# ---------------------------------------------------------------------------
+# inputs of the query RoPE + quantisation step
+# ---------------------------------------------------------------------------
+
+@dataclass
+class QInputs:
+    """Projected queries before RoPE/quantisation and what the step reads."""
+    q: np.ndarray          # uint16 [rows, heads, 128]: bf16 bit patterns
+    positions: np.ndarray  # int32 [rows]
+    cos_sin: np.ndarray    # float32 [max_pos, 64]: cos in [0, 32), sin in [32, 64)
+    w: np.ndarray          # float32 [rows, heads]
+
+
+def rope_table(max_pos: int, base: float = 10000.0) -> np.ndarray:
+    """The rotary table over 64 rotated dimensions: angle(p, i) = p * base^(-i/32)."""
+    inv = base ** (-np.arange(32, dtype=np.float64) / 32.0)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def q_inputs(seed: int, rows: int, heads: int, max_pos: int = 262144,
+             specials: bool = True) -> QInputs:
+    """Seeded bf16 queries ~ N(0, 1) times a per-head gain (log-normal), random
+    positions in [0, max_pos), the rotary table, fp32 weights ~ N(0, 1).  With
+    `specials`, some heads are all zero and some hold values that round to
+    e2m1 ties."""
+    r = _rng(902, seed)
+    gain = np.exp(r.normal(0.0, 1.0, size=(rows, heads, 1))).astype(np.float32)
+    x = (r.standard_normal((rows, heads, DIM), dtype=np.float32) * gain).astype(np.float32)
+    if specials and rows * heads >= 4:
+        flat = x.reshape(-1, DIM)
+        flat[0] = 0.0
+        # exact grid values and midpoints of a group whose scale is 1 (amax 6)
+        ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], dtype=np.float32)
+        flat[1, 64:96] = np.resize(np.concatenate([ties, -ties]), 32)
+        flat[2, :] = np.float32(1e-30)
+    u = x.view(np.uint32)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)   # to bf16 (nearest even)
+    pos = r.integers(0, max_pos, size=rows).astype(np.int32)
+    if rows:
+        pos[0] = 0
+    w = r.standard_normal((rows, heads), dtype=np.float32)
+    return QInputs(bits, pos, rope_table(max_pos), w)
