@@ -105,6 +105,37 @@ def measured_traffic(config):
         return None
 
 
+def time_q_rope_quant(rows, heads, reps=20):
+    """The step before the score calls (RoPE + MXFP4 quantisation of one layer's
+    queries) at the chunk's shape, timed apart from the chunk: device-side random
+    bf16 queries, the rotary table of 262144 positions."""
+    import numpy as np
+    import torch
+    import two_level_top_amd as t
+    import workloads
+    g = torch.Generator(device="cuda").manual_seed(1)
+    q = torch.randn((rows, heads, 128), device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+    pos = torch.randint(0, 262144, (rows,), device="cuda", generator=g, dtype=torch.int32)
+    cs = torch.from_numpy(workloads.rope_table(262144)).cuda()
+    w = torch.randn((rows, heads), device="cuda", generator=g)
+    vals = torch.empty((rows, heads, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, heads, 4), dtype=torch.uint8, device="cuda")
+    w_out = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
+    run = lambda: t.idx_q_rope_quant(q, pos, cs, w, True, 128 ** -0.5, heads ** -0.5, vals, scales, w_out)
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = rows * heads * (256 + 4 + 64 + 4 + 4)   # bf16 query + w in; codes, scales, w out
+    return {"ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "note": "query RoPE + MXFP4 quantisation before the chunk, timed apart from it"}
+
+
 def cpu_baseline(wl, n_rows):
     """The oracle, as it stands, on n_rows evenly spaced rows of the same chunk."""
     import numpy as np
@@ -206,6 +237,7 @@ def main():
         "consumer_topk_rows": {"ms": round(float(np.mean(t_tr)), 4),
                                "GB/s": round(work["topk_rows_bytes"] / (np.mean(t_tr) * 1e-3) / 1e9, 1)},
     }
+    kernels["q_rope_quant"] = time_q_rope_quant(wl.rows, wl.heads)
     out = {
         "metric": METRIC,
         "value": round(wl.rows / (ms * 1e-3), 1),

@@ -178,6 +178,31 @@ idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_ro
                            float* S, int64_t ld, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * idx_q_rope_quant -- the step before the score calls: RoPE, MXFP4
+ * quantisation and head-weight scaling of one layer's projected queries (the
+ * vLLM indexer page, rope_quant_q / fused_indexer_q_rope_quant; on the fp4
+ * path the query scales stay with the query).  Its outputs are an idx_query.
+ *   q         bf16 bits [rows][heads][128]     projected queries
+ *   positions i32 [rows]                       position of each row's token
+ *   cos_sin   f32 [max_pos][64]                cos in [0, 32), sin in [32, 64)
+ *   w         f32 [rows][heads]                head weights before scaling
+ *   is_neox   1: rotate pairs (i, i + 32); 0: pairs (2i, 2i + 1), i < 32
+ * For each (row, head): dimensions 0..63 rotated, r0 = bf16(x0 cos - x1 sin),
+ * r1 = bf16(x1 cos + x0 sin) with separate fp32 products and sums;
+ * dimensions 64..127 unchanged.  Per 32-element group: scale
+ * 2^ceil(log2(fp32(max(amax, 1e-10) * fp32(1/6)))), codes = e2m1 nearest to
+ * x / scale (ties to the even code, saturated at 6, -0 written as 0).
+ *   vals   u8 [rows][heads][64], scales u8 [rows][heads][4] (idx_query layout)
+ *   w_out  f32 [rows][heads] = (w * softmax_scale) * head_scale
+ * Alignment: q and cos_sin 16 bytes; vals, w, w_out 4 bytes.  1 <= heads <=
+ * 64.  Device precondition (clamped, not checked): 0 <= positions < max_pos.
+ */
+idx_status idx_q_rope_quant(const uint16_t* q, const int32_t* positions, const float* cos_sin,
+                            int32_t max_pos, const float* w, int32_t rows, int32_t heads,
+                            int32_t is_neox, float softmax_scale, float head_scale, uint8_t* vals,
+                            uint8_t* scales, float* w_out, hipStream_t stream);
+
+/*
  * idx_amax8_varlen -- block keys (the block_amax.cuh contract quoted in the
  * prefill PR's review thread, and "Level one" of its Design):
  *   keys[r * ldk + i] = max(S[r*ld + 8i .. 8i+7]) for i < nblk - 1,

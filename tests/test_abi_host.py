@@ -127,6 +127,22 @@ def test_score_dense_keys_validation(lib):
     assert f(P(q0), P(kp), P(r0), None, 1024, None, 128, 0, None, 0, None) == 0       # nothing to do
 
 
+def test_q_rope_quant_validation(lib):
+    f = lib.idx_q_rope_quant
+    args = lambda **kw: [kw.get("q", FAKE), FAKE, kw.get("cs", FAKE), kw.get("maxpos", 16), FAKE,
+                         kw.get("rows", 4), kw.get("heads", 8), kw.get("neox", 1),
+                         ctypes.c_float(1.0), ctypes.c_float(1.0), kw.get("vals", FAKE), FAKE, FAKE, None]
+    assert f(*args(rows=-1)) == -1
+    assert f(*args(heads=65)) == -4
+    assert f(*args(maxpos=0)) == -1
+    assert f(*args(neox=2)) == -1
+    assert f(*args(q=None)) == -1
+    assert f(*args(q=FAKE_ODD)) == -2            # 16-byte alignment of q
+    assert f(*args(cs=FAKE_ODD)) == -2
+    assert f(*args(vals=FAKE_ODD2)) == -2
+    assert f(*args(rows=0, q=None)) == 0            # nothing to do
+
+
 def test_tail_validation(lib):
     t, q, kp, rows, tbl = _structs()
     P = ctypes.byref

@@ -199,6 +199,33 @@ def test_fold_workspace(idx, name):
 
 
 # ---------------------------------------------------------------------------
+# idx_q_rope_quant: the step before the score calls (bit-exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,heads,neox", [(37, 64, True), (37, 64, False), (5, 8, True),
+                                             (9, 24, False), (16384, 64, True)])
+def test_q_rope_quant_bitexact(idx, rows, heads, neox):
+    from oracle import q_quant
+    inp = workloads.q_inputs(rows + heads, rows, heads, max_pos=262144 if rows > 1000 else 4096)
+    say(f"q rope quant rows={rows} heads={heads} neox={neox}")
+    q = torch.from_numpy(inp.q.view(np.int16)).cuda()
+    vals = torch.full((rows, heads, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, heads, 4), 0xAB, dtype=torch.uint8, device="cuda")
+    w_out = torch.full((rows, heads), float("nan"), dtype=torch.float32, device="cuda")
+    softmax_scale, head_scale = 128 ** -0.5, heads ** -0.5
+    idx.idx_q_rope_quant(q, dev(inp.positions), dev(inp.cos_sin), dev(inp.w), neox, softmax_scale,
+                         head_scale, vals, scales, w_out)
+    sample = np.arange(rows) if rows <= 64 else np.unique(np.concatenate(
+        [np.arange(8), np.linspace(0, rows - 1, 120).astype(int), [rows - 1]]))
+    v_o, s_o, w_o = q_quant.q_rope_quant(inp.q[sample], inp.positions[sample], inp.cos_sin,
+                                         inp.w[sample], neox, softmax_scale, head_scale)
+    idx_t = torch.from_numpy(sample).cuda()
+    assert np.array_equal(host(vals[idx_t]), v_o), "codes differ"
+    assert np.array_equal(host(scales[idx_t]), s_o), "scales differ"
+    assert np.array_equal(host(w_out[idx_t]).view(np.uint32), w_o.view(np.uint32)), "weights differ"
+
+
+# ---------------------------------------------------------------------------
 # idx_score_dense_keys: the fused source pass
 # ---------------------------------------------------------------------------
 

@@ -5,7 +5,8 @@ current HIP stream out to the C ABI of include/idx.h.  Every step runs in the
 library's HIP kernels; there is no fallback.  If libidx.so has not been built
 (``python -c "import __graft_entry__ as g; g.build()"``), every call raises.
 
-Names follow the C ABI: idx_score_dense, idx_score_dense_keys, idx_amax8_varlen, idx_topk_blocks,
+Names follow the C ABI: idx_score_dense, idx_score_dense_keys, idx_q_rope_quant,
+idx_amax8_varlen, idx_topk_blocks,
 idx_expand_candidates, idx_score_sparse_paged, idx_topk_rows,
 idx_prefill_tail.
 """
@@ -19,7 +20,7 @@ import torch
 
 __all__ = [
     "IdxError", "Query", "KPool", "Rows", "Table", "load",
-    "idx_score_dense", "idx_score_dense_keys", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
+    "idx_score_dense", "idx_score_dense_keys", "idx_q_rope_quant", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
     "idx_score_sparse_paged", "idx_topk_rows", "idx_prefill_tail", "idx_workspace_bytes",
     "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table", "score_workspace",
 ]
@@ -77,6 +78,7 @@ def load():
     sig = {
         "idx_score_dense": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_amax8_varlen": [_P, _I64, _P, _I32, _P, _I64, _I32, _P],
+        "idx_q_rope_quant": [_P, _P, _P, _I32, _P, _I32, _I32, _I32, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P],
         "idx_score_dense_keys": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P, _I64, _I32, _P, ctypes.c_size_t, _P],
         "idx_topk_blocks": [_P, _I64, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
         "idx_expand_candidates": [ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), ctypes.POINTER(_Table), _P],
@@ -283,6 +285,28 @@ def idx_score_dense_keys(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, keys:
                                        _ptr(S), S.stride(0), _ptr(keys), keys.stride(0),
                                        int(skip_le_blocks), _ptr(ws), ws.numel(), _stream(stream)),
            "idx_score_dense_keys")
+
+
+def idx_q_rope_quant(q_bits: torch.Tensor, positions: torch.Tensor, cos_sin: torch.Tensor,
+                     w: torch.Tensor, is_neox: bool, softmax_scale: float, head_scale: float,
+                     vals: torch.Tensor, scales: torch.Tensor, w_out: torch.Tensor, stream=None):
+    """q_bits: bf16 bit patterns as int16 [rows, heads, 128]; outputs an idx_query's arrays."""
+    _req(q_bits, torch.int16, "q"); _req(positions, torch.int32, "positions")
+    _req(cos_sin, torch.float32, "cos_sin"); _req(w, torch.float32, "w")
+    _req(vals, torch.uint8, "vals"); _req(scales, torch.uint8, "scales"); _req(w_out, torch.float32, "w_out")
+    rows, heads = int(q_bits.shape[0]), int(q_bits.shape[1])
+    shapes = {"q": (q_bits, (rows, heads, 128)), "positions": (positions, (rows,)),
+              "w": (w, (rows, heads)), "vals": (vals, (rows, heads, 64)),
+              "scales": (scales, (rows, heads, 4)), "w_out": (w_out, (rows, heads))}
+    for name, (t, shape) in shapes.items():
+        if tuple(t.shape) != shape:
+            raise IdxError(f"{name}: shape {tuple(t.shape)}, expected {shape}")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != 64:
+        raise IdxError("cos_sin must be [max_pos, 64]")
+    _check(load().idx_q_rope_quant(_ptr(q_bits), _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]),
+                                   _ptr(w), rows, heads, 1 if is_neox else 0, float(softmax_scale),
+                                   float(head_scale), _ptr(vals), _ptr(scales), _ptr(w_out),
+                                   _stream(stream)), "idx_q_rope_quant")
 
 
 def idx_amax8_varlen(S, lens, keys, skip_le_blocks: int = 0, stream=None):

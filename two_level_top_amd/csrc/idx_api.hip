@@ -172,6 +172,27 @@ idx_status idx_score_dense_keys(const idx_query* q, const idx_kpool* kp, const i
   return score_dense_impl(q, kp, rows, S, ld, keys, ldk, skip_le_blocks, ws, ws_bytes, stream, fn);
 }
 
+idx_status idx_q_rope_quant(const uint16_t* q, const int32_t* positions, const float* cos_sin,
+                            int32_t max_pos, const float* w, int32_t rows, int32_t heads,
+                            int32_t is_neox, float softmax_scale, float head_scale, uint8_t* vals,
+                            uint8_t* scales, float* w_out, hipStream_t stream) {
+  const char* fn = "idx_q_rope_quant";
+  if (rows < 0) return fail(IDX_E_ARG, "%s: rows < 0", fn);
+  if (heads < 1 || heads > 64) return fail(IDX_E_UNSUPPORTED, "%s: heads %d (1..64)", fn, heads);
+  if (max_pos < 1) return fail(IDX_E_ARG, "%s: max_pos < 1", fn);
+  if (is_neox != 0 && is_neox != 1) return fail(IDX_E_ARG, "%s: is_neox must be 0 or 1", fn);
+  if (rows == 0) return ok();
+  if (!q || !positions || !cos_sin || !w || !vals || !scales || !w_out)
+    return fail(IDX_E_ARG, "%s: a pointer is NULL", fn);
+  if (!aligned(q, 16)) return fail(IDX_E_ALIGN, "%s: q must be 16-byte aligned", fn);
+  if (!aligned(cos_sin, 16)) return fail(IDX_E_ALIGN, "%s: cos_sin must be 16-byte aligned", fn);
+  if (!aligned(vals, 4) || !aligned(w, 4) || !aligned(w_out, 4))
+    return fail(IDX_E_ALIGN, "%s: vals, w and w_out must be 4-byte aligned", fn);
+  return hip_status(idxk::launch_q_rope_quant(q, positions, cos_sin, max_pos, w, rows, heads, is_neox == 1,
+                                              softmax_scale, head_scale, vals, scales, w_out, stream),
+                    fn);
+}
+
 idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int32_t rows,
                             float* keys, int64_t ldk, int32_t skip_le_blocks, hipStream_t stream) {
   const char* fn = "idx_amax8_varlen";

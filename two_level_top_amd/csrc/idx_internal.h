@@ -82,6 +82,10 @@ hipError_t launch_tail_gather(const int32_t* src_rows, int tail_rows, int kb,
                               hipStream_t st);
 
 size_t schedule_bytes(int rows, int kb);
+hipError_t launch_q_rope_quant(const uint16_t* q, const int32_t* positions, const float* cos_sin,
+                               int max_pos, const float* w, int rows, int heads, bool neox,
+                               float softmax_scale, float head_scale, uint8_t* vals,
+                               uint8_t* scales, float* w_out, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // device helpers
