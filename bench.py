@@ -59,7 +59,7 @@ def workload(name):
     raise SystemExit(f"unknown config {name}")
 
 
-def algorithmic_work(wl):
+def algorithmic_work(wl, score_bytes=4):
     """Per-launch algorithmic flops / bytes of each kernel for this workload."""
     import numpy as np
     lens = wl.lens.astype(np.int64)
@@ -76,7 +76,7 @@ def algorithmic_work(wl):
         "topk_blocks_bytes": float((4 * nblk[keyed]).sum() + 4 * wl.kb * wl.rows),
         "sparse_flops": float(flop_per_logit * valid.sum()),
         "sparse_gather_bytes": float(68 * valid.sum()),
-        "topk_rows_bytes": float(4 * valid.sum() + 4 * wl.kc * wl.rows),
+        "topk_rows_bytes": float(score_bytes * valid.sum() + 4 * wl.kc * wl.rows),
     }
 
 
@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "tiny"])
     ap.add_argument("--cpu-rows", type=int, default=192,
                     help="rows of the CPU oracle sample (0 = skip the CPU baseline)")
+    ap.add_argument("--consumer-bf16", action="store_true",
+                    help="the bf16 consumer-score variant (scores and their top-k in bf16)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a device-to-device copy of this many MiB (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -187,7 +189,7 @@ def main():
         return
     wl, desc = workload(args.config)
     print(f"[bench] workload ready: {desc}", file=sys.stderr, flush=True)
-    ch = Chunk(wl)
+    ch = Chunk(wl, consumer_bf16=args.consumer_bf16)
     torch.cuda.synchronize()
     for i in range(args.warmup):
         ch.run()
@@ -206,7 +208,7 @@ def main():
     ms = (t1 - t0) * 1000.0 / args.steps
     print(f"[bench] {args.steps} timed steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
 
-    work = algorithmic_work(wl)
+    work = algorithmic_work(wl, score_bytes=2 if args.consumer_bf16 else 4)
     ncons = len(ch.cons_top)
 
     def avg(a, b):
@@ -252,7 +254,8 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": desc, "rows": wl.rows, "heads": wl.heads, "kb": wl.kb,
-                   "topk": wl.kc, "consumers": ncons},
+                   "topk": wl.kc, "consumers": ncons,
+                   "consumer_scores": "bf16" if args.consumer_bf16 else "fp32"},
         "roofline": {"bound": "mfma", "kernel": dense_name,
                      "achieved": round(dense_tflops, 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_FP4_TFLOPS, 4),

@@ -274,6 +274,19 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
                                   float* T, int64_t ld, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
 
+/*
+ * idx_score_sparse_paged_bf16 -- the same scores written as bf16 (the
+ * prefill PR's consumer output, "Level two": bf16 [tokens, 2048 x 8]): each
+ * element is the fp32 score of idx_score_sparse_paged rounded to the nearest
+ * bf16 (ties to even).  T holds bf16 bit patterns, 2-byte aligned; all else as
+ * above.  A variant: selections made from it agree with the fp32 ones only
+ * up to the bf16 rounding (the PR's test asks for >= 95% agreement and every
+ * disagreement within 2^-5 relative of the selection floor).
+ */
+idx_status idx_score_sparse_paged_bf16(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
+                                       uint16_t* T, int64_t ld, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
 /* Column modes of idx_topk_rows. */
 enum {
   IDX_COLS_IDENTITY = 0,  /* column c is position c, value X[c]                   */
@@ -304,6 +317,17 @@ idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32
                          int32_t k, int mode, const int32_t* blocks, int32_t kb,
                          const int32_t* pos_offset, int32_t* out, void* ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/*
+ * idx_topk_rows_bf16 -- idx_topk_rows over bf16 values (bit patterns, 2-byte
+ * aligned; the prefill PR's topk_transform_bf16_small over a consumer's bf16
+ * scores).  Values compare as the fp32 numbers they are exactly; same modes,
+ * tie rule, outputs and errors.
+ */
+idx_status idx_topk_rows_bf16(const uint16_t* X, int64_t ld, const int32_t* valid, int32_t rows,
+                              int32_t k, int mode, const int32_t* blocks, int32_t kb,
+                              const int32_t* pos_offset, int32_t* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /*
  * idx_prefill_tail -- restrict a published table to the last tail_len[j] rows

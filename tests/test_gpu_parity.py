@@ -376,6 +376,36 @@ def test_topk_rows_blockmap_and_gather(idx, kb, k):
     assert np.array_equal(host(out2), ref2)
 
 
+@pytest.mark.parametrize("kb,k", [(2048, 512), (16, 32), (64, 8)])
+def test_topk_rows_bf16_bitexact(idx, kb, k):
+    """The bf16 top-k against the oracle's top-k of the same (bf16) values;
+    bf16 has few distinct values, so there are many exact ties."""
+    rows = 24
+    nblk_max = 4 * kb + 5
+    blocks, nk = _random_blocks(kb + 7, rows, kb, nblk_max)
+    valid = np.maximum(nk * 8 - (np.arange(rows) % 8), 0).astype(np.int32)
+    valid[nk == 0] = 0
+    Tbits, Tval = workloads.to_bf16(workloads.random_matrix(kb + k + 5, rows, kb * 8))
+    Dbits, Dval = workloads.to_bf16(workloads.random_matrix(kb + k + 6, rows, nblk_max * 8))
+    off = (np.arange(rows, dtype=np.int32) * 3).astype(np.int32)
+    pos = oracle.candidate_positions(blocks, valid)
+    bf = lambda bits: torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    say(f"topk_rows bf16 blockmap kb={kb} k={k}")
+    out = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows_bf16(bf(Tbits), dev(valid), k, out, mode=idx.COLS_BLOCKMAP, blocks=dev(blocks),
+                           pos_offset=dev(off))
+    assert np.array_equal(host(out), oracle.topk_positions(Tval, valid, k, colmap=pos, pos_offset=off))
+    say(f"topk_rows bf16 gather kb={kb} k={k}")
+    out2 = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows_bf16(bf(Dbits), dev(valid), k, out2, mode=idx.COLS_GATHER, blocks=dev(blocks))
+    gathered = np.take_along_axis(Dval, np.maximum(pos, 0).astype(np.int64), 1)
+    assert np.array_equal(host(out2), oracle.topk_positions(gathered, valid, k, colmap=pos))
+    say(f"topk_rows bf16 identity width={kb * 8}")
+    out3 = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows_bf16(bf(Tbits), dev(valid), k, out3)
+    assert np.array_equal(host(out3), oracle.topk_positions(Tval, valid, k))
+
+
 # ---------------------------------------------------------------------------
 # idx_expand_candidates + idx_score_sparse_paged
 # ---------------------------------------------------------------------------
@@ -435,6 +465,17 @@ def test_expand_and_sparse_scores(idx, name):
     m = pos[check] >= 0
     assert_close(Tg[check], To, m, f"{name} sparse scores")
     assert np.isnan(Tg[check][~m]).all(), "sparse scores written past valid_len"
+    # the bf16 variant: the fp32 score rounded to bf16, so within half a bf16
+    # step of the oracle's value plus the fp32 tolerance
+    say(f"sparse scores bf16 {name}")
+    Tb = torch.full((wl.rows, wl.kb * 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+    idx.idx_score_sparse_paged_bf16(ch.queries[1], ch.kp, ch.table, Tb)
+    Tbg = host(Tb.float())[check]
+    o = To[m].astype(np.float64)
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(o), 1e-30))) - 8)
+    err = np.abs(Tbg[m].astype(np.float64) - o)
+    assert (err <= half_ulp + ATOL + RTOL * np.abs(o)).all(), f"bf16 scores: worst {err.max():.3g}"
+    assert np.isnan(Tbg[~m]).all(), "bf16 scores written past valid_len"
 
 
 # ---------------------------------------------------------------------------
@@ -490,6 +531,55 @@ def _check_chunk(wl, ch, rows, n_consumers):
                     assert_same_selection(cons_g[c][i], res["consumer_topk"][c][i], score.get, kth, -1,
                                           f"{wl.name} row {r} consumer {c}")
     assert same_blocks >= 0.9 * len(rows), f"only {same_blocks}/{len(rows)} rows kept identical blocks"
+
+
+def _check_bf16_agreement(wl, ch, rows, n_consumers):
+    """The prefill PR's acceptance test of bf16 consumer scores: the selection
+    agrees with the fp32 one on at least 95% of the positions, picks lie inside
+    the candidate blocks, and every disagreement is within 2^-5 relative of the
+    selection floor (the fp32 k-th score)."""
+    res = oracle.run_chunk(wl, row_ids=rows, n_consumers=n_consumers)
+    blocks_g = host(ch.table.blocks)[rows]
+    agree = total = 0
+    for c in range(len(ch.cons_top)):
+        got = host(ch.cons_top[c])[rows]
+        for i, r in enumerate(rows):
+            if not np.array_equal(blocks_g[i], res["blocks"][i]):
+                continue        # a block set that differs at a tie: compared elsewhere
+            off = int(wl.req_start[r])
+            valid = int(res["valid_len"][i])
+            if valid == 0:
+                assert (got[i] == -1).all()
+                continue
+            T_o = res["T"][c][i, :valid]
+            pos = res["positions"][i, :valid] + off
+            score = dict(zip(pos.tolist(), T_o.tolist()))
+            g = set(int(x) for x in got[i] if x != -1)
+            o = set(int(x) for x in res["consumer_topk"][c][i] if x != -1)
+            assert len(g) == len(o)
+            assert g <= set(score), f"row {r}: a pick outside the candidate blocks"
+            floor = kth_largest(T_o, wl.kc)
+            for x in g ^ o:
+                assert abs(score[x] - floor) <= 2.0 ** -5 * abs(floor), (r, x, score[x], floor)
+            agree += len(g & o)
+            total += len(o)
+    assert total > 0 and agree >= 0.95 * total, f"agreement {agree}/{total}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "long"])
+def test_chunk_bf16_consumers(idx, name):
+    from two_level_top_amd.chunk import Chunk
+    if name == "tiny":
+        wl, rows, nc = workloads.tiny(), np.arange(64), None
+    elif name == "decode":
+        wl, rows, nc = workloads.decode(n_consumers=2), np.arange(0, 64, 3), None
+    else:
+        wl, rows, nc = workloads.long_chunk(n_consumers=1), np.array([0, 4096, 16383]), 1
+    say(f"chunk {name} with bf16 consumer scores")
+    ch = Chunk(wl, n_consumers=nc, consumer_bf16=True)
+    ch.run()
+    torch.cuda.synchronize()
+    _check_bf16_agreement(wl, ch, rows, nc)
 
 
 def test_chunk_tiny(idx):

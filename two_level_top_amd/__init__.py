@@ -7,8 +7,8 @@ library's HIP kernels; there is no fallback.  If libidx.so has not been built
 
 Names follow the C ABI: idx_score_dense, idx_score_dense_keys, idx_q_rope_quant,
 idx_amax8_varlen, idx_topk_blocks,
-idx_expand_candidates, idx_score_sparse_paged, idx_topk_rows,
-idx_prefill_tail.
+idx_expand_candidates, idx_score_sparse_paged, idx_score_sparse_paged_bf16, idx_topk_rows,
+idx_topk_rows_bf16, idx_prefill_tail.
 """
 
 from __future__ import annotations
@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "IdxError", "Query", "KPool", "Rows", "Table", "load",
     "idx_score_dense", "idx_score_dense_keys", "idx_q_rope_quant", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
-    "idx_score_sparse_paged", "idx_topk_rows", "idx_prefill_tail", "idx_workspace_bytes",
+    "idx_score_sparse_paged", "idx_score_sparse_paged_bf16", "idx_topk_rows", "idx_topk_rows_bf16",
+    "idx_prefill_tail", "idx_workspace_bytes",
     "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table", "score_workspace",
 ]
 
@@ -84,6 +85,8 @@ def load():
         "idx_expand_candidates": [ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), ctypes.POINTER(_Table), _P],
         "idx_score_sparse_paged": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_topk_rows": [_P, _I64, _P, _I32, _I32, ctypes.c_int, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+        "idx_topk_rows_bf16": [_P, _I64, _P, _I32, _I32, ctypes.c_int, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+        "idx_score_sparse_paged_bf16": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_prefill_tail": [ctypes.POINTER(_Table), _P, _P, _I32, ctypes.POINTER(_Table), _P, ctypes.c_size_t, _P],
     }
     for name, args in sig.items():
@@ -340,6 +343,35 @@ def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=
                                          _ptr(T), T.stride(0), _ptr(ws), ws.numel(),
                                          _stream(stream)),
            "idx_score_sparse_paged")
+
+
+def idx_score_sparse_paged_bf16(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=None,
+                                stream=None):
+    """T: torch.bfloat16 [rows, >= kb * 8]."""
+    _req(T, torch.bfloat16, "T")
+    ws = _score_ws(ws, q.rows, T.device, stream)
+    q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
+    _check(load().idx_score_sparse_paged_bf16(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
+                                              _ptr(T), T.stride(0), _ptr(ws), ws.numel(),
+                                              _stream(stream)),
+           "idx_score_sparse_paged_bf16")
+
+
+def idx_topk_rows_bf16(X, valid, k: int, out, mode: int = COLS_IDENTITY, blocks=None,
+                       pos_offset=None, stream=None):
+    """X: torch.bfloat16 rows; as idx_topk_rows otherwise."""
+    _req(X, torch.bfloat16, "X"); _req(valid, torch.int32, "valid"); _req(out, torch.int32, "out")
+    if out.shape[-1] != k:
+        raise IdxError("out must be [rows, k]")
+    kb = 0
+    if blocks is not None:
+        _req(blocks, torch.int32, "blocks")
+        kb = int(blocks.shape[-1])
+    if pos_offset is not None:
+        _req(pos_offset, torch.int32, "pos_offset")
+    _check(load().idx_topk_rows_bf16(_ptr(X), X.stride(0), _ptr(valid), int(valid.shape[0]), k, mode,
+                                     _ptr(blocks), kb, _ptr(pos_offset), _ptr(out), None, 0,
+                                     _stream(stream)), "idx_topk_rows_bf16")
 
 
 def idx_topk_rows(X, valid, k: int, out, mode: int = COLS_IDENTITY, blocks=None, pos_offset=None,

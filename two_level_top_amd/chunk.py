@@ -30,8 +30,8 @@ import torch
 
 from . import (COLS_BLOCKMAP, COLS_GATHER, COLS_IDENTITY, KPool, Query, Rows, Table,
                idx_amax8_varlen, idx_expand_candidates, idx_score_dense, idx_score_dense_keys,
-               idx_score_sparse_paged, idx_topk_blocks, idx_topk_rows, score_workspace,
-               stream_wait_table)
+               idx_score_sparse_paged, idx_score_sparse_paged_bf16, idx_topk_blocks, idx_topk_rows,
+               idx_topk_rows_bf16, score_workspace, stream_wait_table)
 
 
 def _dev(a, dtype, device):
@@ -42,9 +42,10 @@ class Chunk:
     """Device copies of a workload (see the workloads package) and its buffers."""
 
     def __init__(self, wl, device="cuda", n_consumers=None, k_source=None, with_offset=True,
-                 share_T=True, fused_keys=True):
+                 share_T=True, fused_keys=True, consumer_bf16=False):
         self.wl = wl
         self.fused_keys = fused_keys
+        self.consumer_bf16 = consumer_bf16   # consumers write and select bf16 scores
         self.device = device
         self.R, self.kb, self.kc = wl.rows, wl.kb, wl.kc
         self.k_src = wl.kc if k_source is None else k_source
@@ -60,8 +61,8 @@ class Chunk:
         self.table = Table(self.R, self.kb, device)
         ncons = len(self.queries) - 1
         nT = 1 if share_T else max(1, ncons)
-        self.T = [torch.empty((self.R, self.kb * 8), dtype=torch.float32, device=device)
-                  for _ in range(nT)]
+        tdt = torch.bfloat16 if consumer_bf16 else torch.float32
+        self.T = [torch.empty((self.R, self.kb * 8), dtype=tdt, device=device) for _ in range(nT)]
         self.src_top = torch.empty((self.R, self.k_src), dtype=torch.int32, device=device)
         self.cons_top = [torch.empty((self.R, self.kc), dtype=torch.int32, device=device)
                          for _ in range(ncons)]
@@ -118,11 +119,13 @@ class Chunk:
     # -- a consumer layer ---------------------------------------------------
     def consumer(self, i: int):
         T = self.T[i % len(self.T)]
+        score = idx_score_sparse_paged_bf16 if self.consumer_bf16 else idx_score_sparse_paged
+        select = idx_topk_rows_bf16 if self.consumer_bf16 else idx_topk_rows
         self._mark(f"sparse{i}<")
-        idx_score_sparse_paged(self.queries[1 + i], self.kp, self.table, T, ws=self.ws)
+        score(self.queries[1 + i], self.kp, self.table, T, ws=self.ws)
         self._mark(f"sparse{i}>")
-        idx_topk_rows(T, self.table.valid_len, self.kc, self.cons_top[i], mode=COLS_BLOCKMAP,
-                      blocks=self.table.blocks, pos_offset=self.rows.pos_offset)
+        select(T, self.table.valid_len, self.kc, self.cons_top[i], mode=COLS_BLOCKMAP,
+               blocks=self.table.blocks, pos_offset=self.rows.pos_offset)
         self._mark(f"topk_rows{i}>")
 
     def run(self):

@@ -219,7 +219,7 @@ idx_status idx_topk_blocks(const float* keys, int64_t ldk, const int32_t* len, i
   if (ldk < 1) return fail(IDX_E_ARG, "%s: ldk < 1", fn);
   if (rows == 0) return ok();
   if (!keys || !len || !blocks || !n_kept) return fail(IDX_E_ARG, "%s: a pointer is NULL", fn);
-  return hip_status(idxk::launch_topk(3, keys, ldk, nullptr, len, rows, kb, ldk, nullptr, kb,
+  return hip_status(idxk::launch_topk(3, keys, false, ldk, nullptr, len, rows, kb, ldk, nullptr, kb,
                                       nullptr, blocks, n_kept, stream), fn);
 }
 
@@ -240,10 +240,9 @@ idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_
   return ok();
 }
 
-idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
-                                  float* T, int64_t ld, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
-  const char* fn = "idx_score_sparse_paged";
+static idx_status score_sparse_impl(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
+                                    void* T, int64_t ld, bool bf16, void* ws, size_t ws_bytes,
+                                    hipStream_t stream, const char* fn) {
   TRY(check_query(q, fn));
   TRY(check_pool(kp, fn, false));
   TRY(check_table(tbl, fn, true));
@@ -253,11 +252,11 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
   if ((int64_t)kp->num_pages * idxk::kPageBytes > 0xffffffffLL)
     return fail(IDX_E_UNSUPPORTED, "%s: pool of %d pages exceeds 4 GiB", fn, kp->num_pages);
   if (tbl->rows > 0 && !T) return fail(IDX_E_ARG, "%s: T is NULL", fn);
-  if (!aligned(T, 4)) return fail(IDX_E_ALIGN, "%s: T must be 4-byte aligned", fn);
+  if (!aligned(T, bf16 ? 2 : 4)) return fail(IDX_E_ALIGN, "%s: T must be %d-byte aligned", fn, bf16 ? 2 : 4);
   TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
   if (tbl->ready) {
     hipError_t e = hipStreamWaitEvent(stream, tbl->ready, 0);
-    if (e != hipSuccess) return hip_status(e, "idx_score_sparse_paged: hipStreamWaitEvent");
+    if (e != hipSuccess) return hip_status(e, "hipStreamWaitEvent on the table's ready event");
   }
   if (tbl->rows == 0) return ok();
   idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
@@ -266,15 +265,25 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
   if (e != hipSuccess) return hip_status(e, fn);
   return hip_status(idxk::launch_score_sparse(qa, fold, kp->pool, kp->num_pages, tbl->phys, tbl->n_kept,
                                               tbl->valid_len, tbl->rows, tbl->kb, tbl->schedule, T,
-                                              ld, stream), fn);
+                                              ld, bf16, stream), fn);
 }
 
-idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32_t rows, int32_t k,
-                         int mode, const int32_t* blocks, int32_t kb, const int32_t* pos_offset,
-                         int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  const char* fn = "idx_topk_rows";
-  (void)ws;
-  (void)ws_bytes;
+idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
+                                  float* T, int64_t ld, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  return score_sparse_impl(q, kp, tbl, T, ld, false, ws, ws_bytes, stream, "idx_score_sparse_paged");
+}
+
+idx_status idx_score_sparse_paged_bf16(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
+                                       uint16_t* T, int64_t ld, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  return score_sparse_impl(q, kp, tbl, T, ld, true, ws, ws_bytes, stream, "idx_score_sparse_paged_bf16");
+}
+
+static idx_status topk_rows_impl(const void* X, bool bf16, int64_t ld, const int32_t* valid,
+                                 int32_t rows, int32_t k, int mode, const int32_t* blocks, int32_t kb,
+                                 const int32_t* pos_offset, int32_t* out, hipStream_t stream,
+                                 const char* fn) {
   if (rows < 0) return fail(IDX_E_ARG, "%s: rows < 0", fn);
   if (k < 1) return fail(IDX_E_ARG, "%s: k < 1", fn);
   if (ld < 1) return fail(IDX_E_ARG, "%s: ld < 1", fn);
@@ -288,10 +297,30 @@ idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32
   }
   if (rows == 0) return ok();
   if (!X || !valid || !out) return fail(IDX_E_ARG, "%s: X/valid/out is NULL", fn);
+  if (!aligned(X, bf16 ? 2 : 4)) return fail(IDX_E_ALIGN, "%s: X must be %d-byte aligned", fn, bf16 ? 2 : 4);
   // widest row the call can see: ld columns, or kb * 8 candidate columns
   const int64_t width = mode == IDX_COLS_IDENTITY ? ld : (int64_t)kb * idxk::kBlock;
-  return hip_status(idxk::launch_topk(mode, X, ld, valid, nullptr, rows, k, width, blocks, kb,
+  return hip_status(idxk::launch_topk(mode, X, bf16, ld, valid, nullptr, rows, k, width, blocks, kb,
                                       pos_offset, out, nullptr, stream), fn);
+}
+
+idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32_t rows, int32_t k,
+                         int mode, const int32_t* blocks, int32_t kb, const int32_t* pos_offset,
+                         int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return topk_rows_impl(X, false, ld, valid, rows, k, mode, blocks, kb, pos_offset, out, stream,
+                        "idx_topk_rows");
+}
+
+idx_status idx_topk_rows_bf16(const uint16_t* X, int64_t ld, const int32_t* valid, int32_t rows,
+                              int32_t k, int mode, const int32_t* blocks, int32_t kb,
+                              const int32_t* pos_offset, int32_t* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return topk_rows_impl(X, true, ld, valid, rows, k, mode, blocks, kb, pos_offset, out, stream,
+                        "idx_topk_rows_bf16");
 }
 
 idx_status idx_prefill_tail(const idx_table* full, const int32_t* rows_per_req_host,

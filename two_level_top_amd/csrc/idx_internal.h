@@ -55,7 +55,8 @@ hipError_t launch_amax8(const float* S, int64_t ld, const int32_t* len, int rows
                         int64_t ldk, int skip, hipStream_t st);
 
 // mode: 0 identity, 1 blockmap, 2 gather, 3 block keys (idx_topk_blocks)
-hipError_t launch_topk(int mode, const float* X, int64_t ld, const int32_t* nvalid,
+// bf16: X holds bf16 values (modes 0-2)
+hipError_t launch_topk(int mode, const void* X, bool bf16, int64_t ld, const int32_t* nvalid,
                        const int32_t* len_for_blocks, int rows, int k, int64_t max_cols,
                        const int32_t* blocks, int kb, const int32_t* pos_offset, int32_t* out,
                        int32_t* n_kept, hipStream_t st);
@@ -72,7 +73,7 @@ hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const ui
                                int num_pages,
                                const int32_t* phys, const int32_t* n_kept,
                                const int32_t* valid_len, int rows, int kb, const void* schedule,
-                               float* T, int64_t ld, hipStream_t st);
+                               void* T, int64_t ld, bool bf16, hipStream_t st);
 
 hipError_t launch_tail_gather(const int32_t* src_rows, int tail_rows, int kb,
                               const int32_t* blocks, const int32_t* n_kept, const int32_t* phys,

@@ -52,7 +52,14 @@ __device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t pool, int bov,
   }
 }
 
-template <int HB>
+// nearest bf16 of a finite fp32 value (ties to even), as its 16 bits
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// BF16: scores are written as bf16 (the prefill PR's consumer output dtype)
+template <int HB, bool BF16>
 __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
                                                            const uint8_t* __restrict__ fold,
                                                            const uint8_t* __restrict__ pool,
@@ -61,7 +68,7 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
                                                            const int32_t* __restrict__ n_kept,
                                                            const int32_t* __restrict__ valid_len,
                                                            int kb, const int32_t* __restrict__ sched,
-                                                           float* __restrict__ T, int64_t ld,
+                                                           void* __restrict__ T, int64_t ld,
                                                            int upw, int split) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -100,7 +107,9 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
     const int sov = (int)(pgo + kPageValBytes + (uint32_t)(pb & 7) * (kBlock * kScaleBytes));
     // valid columns of this unit: stores past them are dropped by the resource
     const int ncols = max(0, min(vl - first * kBlock, nblk * kBlock));
-    const __amdgpu_buffer_rsrc_t trs = buffer_rsrc(T + (int64_t)row * ld + first * kBlock, (uint32_t)ncols * 4u);
+    constexpr uint32_t kEl = BF16 ? 2u : 4u;   // bytes per score
+    const __amdgpu_buffer_rsrc_t trs = buffer_rsrc(static_cast<char*>(T) + ((int64_t)row * ld + first * kBlock) * kEl,
+                                                   (uint32_t)ncols * kEl);
     const int ngroups = (nblk + 7) / 8;
     auto sel_of = [&](int g) { return 4 * min(8 * g + half, nblk - 1); };
     auto compute = [&](int g, const GroupOps& cur) {
@@ -112,7 +121,10 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
         p[t] = tile_epilogue<HB>(f, acc);
       }
       const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), trs, (uint32_t)(g * 64 + lane) * 4u, 0, 0);
+      if (BF16)
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(tot), trs, (uint32_t)(g * 64 + lane) * kEl, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), trs, (uint32_t)(g * 64 + lane) * kEl, 0, 0);
     };
     const int g0 = part * gper;
     const int g1 = min(ngroups, g0 + gper);
@@ -133,7 +145,7 @@ hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const ui
                                int num_pages,
                                const int32_t* phys, const int32_t* n_kept,
                                const int32_t* valid_len, int rows, int kb, const void* schedule,
-                               float* T, int64_t ld, hipStream_t st) {
+                               void* T, int64_t ld, bool bf16, hipStream_t st) {
   const int64_t max_units = (int64_t)rows * ((kb + kUnitBlocks - 1) / kUnitBlocks);
   if (max_units <= 0) return hipSuccess;
   int upw = 1, split = 1;
@@ -148,12 +160,25 @@ hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const ui
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int32_t* sched = static_cast<const int32_t*>(schedule);
   const int hb = (q.heads + 15) / 16;
-  switch (hb) {
-    case 1: hipLaunchKernelGGL(score_sparse_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
-    case 2: hipLaunchKernelGGL(score_sparse_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
-    case 3: hipLaunchKernelGGL(score_sparse_kernel<3>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
-    default: hipLaunchKernelGGL(score_sparse_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split); break;
+#define IDX_SPARSE_LAUNCH(H, B)                                                                        \
+  hipLaunchKernelGGL((score_sparse_kernel<H, B>), dim3((unsigned)grid), dim3(256), 0, st, q, fold, pool, \
+                     num_pages, phys, n_kept, valid_len, kb, sched, T, ld, upw, split)
+  if (bf16) {
+    switch (hb) {
+      case 1: IDX_SPARSE_LAUNCH(1, true); break;
+      case 2: IDX_SPARSE_LAUNCH(2, true); break;
+      case 3: IDX_SPARSE_LAUNCH(3, true); break;
+      default: IDX_SPARSE_LAUNCH(4, true); break;
+    }
+  } else {
+    switch (hb) {
+      case 1: IDX_SPARSE_LAUNCH(1, false); break;
+      case 2: IDX_SPARSE_LAUNCH(2, false); break;
+      case 3: IDX_SPARSE_LAUNCH(3, false); break;
+      default: IDX_SPARSE_LAUNCH(4, false); break;
+    }
   }
+#undef IDX_SPARSE_LAUNCH
   return hipGetLastError();
 }
 

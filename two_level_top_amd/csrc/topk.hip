@@ -52,7 +52,7 @@ constexpr uint32_t kNegInf = 0x007fffffu;              // order_key(-inf)
 enum { MODE_IDENTITY = 0, MODE_BLOCKMAP = 1, MODE_GATHER = 2, MODE_KEYS = 3 };
 
 struct TopkArgs {
-  const float* X;
+  const void* X;           // float, or bf16 bits for the BF16 kernels
   int64_t ld;
   const int32_t* nvalid;   // columns per row (modes 0-2)
   const int32_t* len;      // compress_len per row (mode 3: nblk = ceil(len / 8))
@@ -123,9 +123,16 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// element e of a row as fp32 (exact for bf16)
+template <bool BF16>
+__device__ __forceinline__ float elem(const void* Xr, int64_t e) {
+  if (BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(Xr)[e] << 16);
+  return static_cast<const float*>(Xr)[e];
+}
+
 // 4 consecutive values starting at element i (i % 4 == 0) of the row.
-template <int MODE, bool VEC>
-__device__ __forceinline__ void load4(const TopkArgs& a, const float* Xr, const int32_t* blk, int i,
+template <int MODE, bool VEC, bool BF16>
+__device__ __forceinline__ void load4(const TopkArgs& a, const void* Xr, const int32_t* blk, int i,
                                       int n, float (&v)[4]) {
   if (VEC && i + 3 < n) {
     int64_t p = i;
@@ -133,8 +140,14 @@ __device__ __forceinline__ void load4(const TopkArgs& a, const float* Xr, const 
       p = (int64_t)blk[i >> 3] * kBlock + (i & 7);
       if (p < 0 || p + 3 >= a.ld) p = 0;   // outside the contract: stay inside the row
     }
-    const float4 x = *reinterpret_cast<const float4*>(Xr + p);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    if (BF16) {
+      const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Xr) + p);
+      v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
+      v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(Xr) + p);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
     return;
   }
 #pragma unroll
@@ -147,7 +160,7 @@ __device__ __forceinline__ void load4(const TopkArgs& a, const float* Xr, const 
         p = (int64_t)blk[ie >> 3] * kBlock + (ie & 7);
         if (p < 0 || p >= a.ld) p = 0;
       }
-      x = Xr[p];
+      x = elem<BF16>(Xr, p);
     }
     v[e] = x;
   }
@@ -199,7 +212,7 @@ __device__ __forceinline__ int find_bin(TopkShared& sh, uint32_t rem, uint32_t* 
 }
 
 // RESIDENT: every row fits one chunk (n <= THREADS * 64), loaded once.
-template <int MODE, bool VEC, int THREADS, bool RESIDENT>
+template <int MODE, bool VEC, int THREADS, bool RESIDENT, bool BF16>
 __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
   constexpr int W = THREADS / 64;
   constexpr int kChunk = W * kWaveSlice;
@@ -223,7 +236,8 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
   const int32_t pad = MODE == MODE_KEYS ? 0x7fffffff : -1;
   const int32_t off = (MODE != MODE_KEYS && a.pos_offset) ? a.pos_offset[row] : 0;
   const int32_t* blk = (MODE == MODE_BLOCKMAP || MODE == MODE_GATHER) ? a.blocks + (int64_t)row * a.kb : nullptr;
-  const float* Xr = a.X + (int64_t)row * a.ld;
+  const void* Xr = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(a.X) + (int64_t)row * a.ld)
+                        : static_cast<const void*>(static_cast<const float*>(a.X) + (int64_t)row * a.ld);
 
   if (n <= k) {  // every column is kept
     for (int i = tid; i < k; i += THREADS) out[i] = i < n ? map_index<MODE>(blk, i) + off : pad;
@@ -242,7 +256,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
       const int i = c * kChunk + ebase + 256 * j;
       if (MODE == MODE_BLOCKMAP || MODE == MODE_GATHER) bid[j] = i < n ? blk[i >> 3] : 0;
       float v[4];
-      load4<MODE, VEC>(a, Xr, blk, i, n, v);
+      load4<MODE, VEC, BF16>(a, Xr, blk, i, n, v);
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[j][e] = i + e < n ? order_key(v[e]) : 0u;
     }
@@ -459,40 +473,50 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
   if (MODE == MODE_KEYS && tid == 0) a.n_kept[row] = k;
 }
 
-template <int MODE, int THREADS, bool RESIDENT>
+template <int MODE, int THREADS, bool RESIDENT, bool BF16>
 static void launch_sized(const TopkArgs& a, int rows, bool vec, hipStream_t st) {
   if (vec)
-    hipLaunchKernelGGL((topk_kernel<MODE, true, THREADS, RESIDENT>), dim3(rows), dim3(THREADS), 0, st, a);
+    hipLaunchKernelGGL((topk_kernel<MODE, true, THREADS, RESIDENT, BF16>), dim3(rows), dim3(THREADS), 0, st, a);
   else
-    hipLaunchKernelGGL((topk_kernel<MODE, false, THREADS, RESIDENT>), dim3(rows), dim3(THREADS), 0, st, a);
+    hipLaunchKernelGGL((topk_kernel<MODE, false, THREADS, RESIDENT, BF16>), dim3(rows), dim3(THREADS), 0, st, a);
 }
 
 // the workgroup size is chosen from the widest row the call can see
-template <int MODE>
+template <int MODE, bool BF16>
 static void launch_mode(const TopkArgs& a, int rows, int64_t width, bool vec, hipStream_t st) {
   if (width <= 4 * kWaveSlice)
-    launch_sized<MODE, 256, true>(a, rows, vec, st);
+    launch_sized<MODE, 256, true, BF16>(a, rows, vec, st);
   else if (width <= 8 * kWaveSlice)
-    launch_sized<MODE, 512, true>(a, rows, vec, st);
+    launch_sized<MODE, 512, true, BF16>(a, rows, vec, st);
   else if (width <= 16 * kWaveSlice)
-    launch_sized<MODE, 1024, true>(a, rows, vec, st);
+    launch_sized<MODE, 1024, true, BF16>(a, rows, vec, st);
   else
-    launch_sized<MODE, 1024, false>(a, rows, vec, st);
+    launch_sized<MODE, 1024, false, BF16>(a, rows, vec, st);
 }
 
-hipError_t launch_topk(int mode, const float* X, int64_t ld, const int32_t* nvalid,
+hipError_t launch_topk(int mode, const void* X, bool bf16, int64_t ld, const int32_t* nvalid,
                        const int32_t* len_for_blocks, int rows, int k, int64_t max_cols,
                        const int32_t* blocks, int kb, const int32_t* pos_offset, int32_t* out,
                        int32_t* n_kept, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   TopkArgs a{X, ld, nvalid, len_for_blocks, k, blocks, kb, pos_offset, out, n_kept};
-  // 16-byte loads need 16-byte aligned rows
-  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(X) % 16 == 0);
-  switch (mode) {
-    case MODE_IDENTITY: launch_mode<MODE_IDENTITY>(a, rows, max_cols, vec, st); break;
-    case MODE_BLOCKMAP: launch_mode<MODE_BLOCKMAP>(a, rows, max_cols, vec, st); break;
-    case MODE_GATHER: launch_mode<MODE_GATHER>(a, rows, max_cols, vec, st); break;
-    default: launch_mode<MODE_KEYS>(a, rows, max_cols, vec, st); break;
+  // vector loads (4 elements) need rows aligned to them
+  const size_t vbytes = bf16 ? 8 : 16;
+  const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(X) % vbytes == 0);
+  if (bf16) {
+    switch (mode) {
+      case MODE_IDENTITY: launch_mode<MODE_IDENTITY, true>(a, rows, max_cols, vec, st); break;
+      case MODE_BLOCKMAP: launch_mode<MODE_BLOCKMAP, true>(a, rows, max_cols, vec, st); break;
+      case MODE_GATHER: launch_mode<MODE_GATHER, true>(a, rows, max_cols, vec, st); break;
+      default: return hipErrorInvalidValue;   // block keys are fp32
+    }
+  } else {
+    switch (mode) {
+      case MODE_IDENTITY: launch_mode<MODE_IDENTITY, false>(a, rows, max_cols, vec, st); break;
+      case MODE_BLOCKMAP: launch_mode<MODE_BLOCKMAP, false>(a, rows, max_cols, vec, st); break;
+      case MODE_GATHER: launch_mode<MODE_GATHER, false>(a, rows, max_cols, vec, st); break;
+      default: launch_mode<MODE_KEYS, false>(a, rows, max_cols, vec, st); break;
+    }
   }
   return hipGetLastError();
 }

@@ -313,6 +313,14 @@ def random_matrix(seed: int, rows: int, width: int, ties: bool = True,
     return x
 
 
+def to_bf16(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Input construction for bf16 operands: float32 -> (bf16 bit patterns as
+    uint16, the same values as float32), nearest with ties to even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return bits, (bits.astype(np.uint32) << 16).view(np.float32)
+
+
 def random_lengths(seed: int, rows: int, lo: int, hi: int, extra=()) -> np.ndarray:
     """int32 [rows] uniform in [lo, hi], the given values placed first."""
     r = _rng(901, seed)
