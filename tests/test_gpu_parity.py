@@ -406,6 +406,61 @@ def test_topk_rows_bf16_bitexact(idx, kb, k):
     assert np.array_equal(host(out3), oracle.topk_positions(Tval, valid, k))
 
 
+# Rows whose k-th value sits in a crowd.  The selection keeps everything at or
+# above the threshold's histogram bin in an LDS list when that fits, and
+# otherwise refines the bin from an LDS candidate list, or from the registers
+# when that overflows too: the cluster sizes below reach each of these, with
+# and without exact ties at the threshold, in one chunk and across chunks.
+CROWDS = [("constant", 0), ("zeros", 0), ("cluster", 3000), ("cluster", 8000), ("neginf", 0),
+          ("posinf", 0), ("posinf_many", 0)]
+
+
+@pytest.mark.parametrize("width,k", [(16384, 512), (32768, 2048), (1024, 32), (70000, 512)])
+@pytest.mark.parametrize("kind,cluster", CROWDS)
+def test_topk_rows_crowded_threshold(idx, width, k, kind, cluster):
+    rows = 4
+    X = workloads.crowded_rows(width + k + cluster, kind, rows, width, k, cluster)
+    valid = np.array([width, width - 3, k + 1, width // 2], np.int32)
+    say(f"topk_rows crowded {kind}/{cluster} width={width} k={k}")
+    out = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows(dev(X), dev(valid), k, out)
+    assert np.array_equal(host(out), oracle.topk_positions(X, valid, k))
+
+
+@pytest.mark.parametrize("kind,cluster", CROWDS)
+def test_topk_mapped_and_blocks_crowded(idx, kind, cluster):
+    kb, k, rows = 2048, 512, 4
+    nblk_max = 4 * kb + 5
+    blocks, nk = _random_blocks(kb + 11, rows, kb, nblk_max)
+    valid = np.maximum(nk * 8 - (np.arange(rows) % 8), 0).astype(np.int32)
+    valid[nk == 0] = 0
+    pos = oracle.candidate_positions(blocks, valid)
+    T = workloads.crowded_rows(kb + cluster, kind, rows, kb * 8, k, cluster)
+    say(f"topk_rows crowded blockmap {kind}/{cluster}")
+    out = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows(dev(T), dev(valid), k, out, mode=idx.COLS_BLOCKMAP, blocks=dev(blocks))
+    assert np.array_equal(host(out), oracle.topk_positions(T, valid, k, colmap=pos))
+    dense = workloads.crowded_rows(kb + cluster + 1, kind, rows, nblk_max * 8, k, cluster)
+    say(f"topk_rows crowded gather {kind}/{cluster}")
+    out2 = torch.full((rows, k), -9, dtype=torch.int32, device="cuda")
+    idx.idx_topk_rows(dev(dense), dev(valid), k, out2, mode=idx.COLS_GATHER, blocks=dev(blocks))
+    gathered = np.take_along_axis(dense, np.maximum(pos, 0).astype(np.int64), 1)
+    assert np.array_equal(host(out2), oracle.topk_positions(gathered, valid, k, colmap=pos))
+    maxblk = 32768
+    keys = workloads.crowded_rows(kb + cluster + 2, kind, rows, maxblk, kb, cluster)
+    lens = np.array([maxblk * 8, maxblk * 8 - 5, (kb + 1) * 8, maxblk * 4 - 1], np.int32)
+    nblk = oracle.nblocks(lens)
+    for r in range(rows):
+        keys[r, nblk[r] - 1] = np.inf       # a keyed row's newest block
+    say(f"topk_blocks crowded {kind}/{cluster}")
+    bl = torch.full((rows, kb), -5, dtype=torch.int32, device="cuda")
+    n_kept = torch.full((rows,), -5, dtype=torch.int32, device="cuda")
+    idx.idx_topk_blocks(dev(keys), dev(lens), kb, bl, n_kept)
+    bo, no = oracle.select_blocks(keys, lens, kb)
+    assert np.array_equal(host(n_kept), no)
+    assert np.array_equal(host(bl), bo)
+
+
 # ---------------------------------------------------------------------------
 # idx_expand_candidates + idx_score_sparse_paged
 # ---------------------------------------------------------------------------

@@ -135,13 +135,6 @@ __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, f
   return e + f;
 }
 
-// Order-preserving map of fp32 to u32 (-0 folded onto +0).
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Raw buffer resource over [p, p + bytes): accesses past the end are dropped
 // (stores) or read as zero (loads) by the hardware, so ragged edges need no
 // branches.  Dword 3 = 32-bit data format, the raw-buffer setting of gfx9.

@@ -17,27 +17,37 @@
 // streamed in chunks); wave w owns the contiguous 2048-element slice
 // [2048 w, 2048 w + 2048) of a chunk and reads it with coalesced 16-byte
 // loads: in step j lane l holds elements 256 j + 4 l .. 256 j + 4 l + 3, all
-// in one block of 8, whose id is loaded once with them.
-// Values become order-preserving u32 keys (-0 folded onto +0); slots past the
-// row's end get key 0, which lies below -inf, so they are never counted as
-// finite, never compare greater than or equal to a threshold, and only ever
-// land in the -inf bin, below every valid element.
+// in one block of 8.
+// Values become order-preserving u32 keys (x >= +0: bits + 2^31; x < 0: the
+// negated bits, which puts -0 on the key of +0); slots past the row's end get
+// key 0, which lies below -inf, so they are never counted as finite, never
+// compare greater than or equal to a threshold, and only ever land in the
+// -inf bin, below every valid element.  The kernel is bound by its VALU
+// instructions per element, which every pass over the registers keeps to a
+// few.
 //
-//   1. threshold: the k-th largest key K and `need`, the number of elements
-//      equal to K that are selected.  One histogram pass over the digit
+//   1. threshold bin: one histogram pass over the digit
 //      1 + ((key - kmin) >> shift), kmin/kmax being the finite extremes of the
 //      row and shift the smallest one that fits the span in 2046 bins (-inf
 //      gets digit 0, +inf the one above the largest finite digit): one row's
-//      data spreads over the bins, so the LDS atomics rarely collide.  The
-//      keys of the bin holding the k-th largest (a few dozen, typically) are
-//      copied to an LDS list, and up to two more histogram passes (<= 11 bits
-//      each) over that list fix the low bits of K.  A list that would
-//      overflow LDS is refined from the registers instead.
-//   2. ordered compaction: element i is kept iff key > K, or key == K and
-//      fewer than `need` equal keys precede it.  Each wave gets its
-//      predecessors' counts from one 16-entry scan, then walks its slice in
-//      index order with ballots and mbcnt (no further barriers), so the output
-//      comes out in ascending index order with no sort.
+//      data spreads over the bins, so the LDS atomics rarely collide.  The bin
+//      holding the k-th largest key K gives a lower bound for every kept key.
+//   2. list: one ordered pass writes (position, key) of every element at or
+//      above that bound to an LDS list in index order (each wave gets its
+//      predecessors' counts from one 16-entry scan, then walks its slice with
+//      ballots and mbcnt).  The list holds the k - need elements above the
+//      bin plus the bin itself: about k plus a few hundred entries.
+//   3. on the list alone: up to two more histogram passes (<= 11 bits each)
+//      over the bin's entries fix the low bits of K and `need`, the number of
+//      entries equal to K that are selected; then one block-wide scan of the
+//      (greater, equal) counts writes entry e iff key > K, or key == K and
+//      fewer than `need` equal keys precede it -- in list order, which is
+//      ascending index order.
+// A row whose list would not fit LDS (many ties at the threshold, a
+// degenerate value spread) takes the register path instead: the bin's keys
+// go to an LDS candidate list (or are refined straight from the registers if
+// that overflows too), and the ordered compaction runs over the registers
+// with separate greater / equal ballots.
 #include "idx_internal.h"
 
 namespace idxk {
@@ -46,8 +56,9 @@ constexpr int kTopkMaxWaves = 16;
 constexpr int kTopkSteps = 8;                          // 16-byte loads per lane per chunk
 constexpr int kWaveSlice = kTopkSteps * 256;           // 2048
 constexpr int kBins = 2048;                            // 0: -inf, 1..2046 finite, 2047: +inf
-constexpr uint32_t kPosInf = 0xff800000u;              // order_key(+inf)
-constexpr uint32_t kNegInf = 0x007fffffu;              // order_key(-inf)
+constexpr uint32_t kPosInf = 0xff800000u;              // value_key(+inf)
+constexpr uint32_t kNegInf = 0x00800000u;              // value_key(-inf)
+// finite keys lie in [0x00800001, 0xff7fffff]; empty slots are 0
 
 enum { MODE_IDENTITY = 0, MODE_BLOCKMAP = 1, MODE_GATHER = 2, MODE_KEYS = 3 };
 
@@ -64,15 +75,29 @@ struct TopkArgs {
   int32_t* n_kept;         // mode 3
 };
 
-constexpr uint32_t kCand = 4096;   // candidate list of the threshold bin
+constexpr uint32_t kCand = 4096;   // register path: keys of the threshold bin
 
+template <int THREADS>
 struct TopkShared {
+  static constexpr int kList = 4 * THREADS;   // list path: (position, key) pairs
   uint32_t hist[kBins];
-  uint32_t cand[kCand];
+  union {
+    uint32_t cand[kCand];
+    uint32_t list[2 * kList];
+  };
   uint32_t wred[kTopkMaxWaves][2];
   uint32_t wcnt[kTopkMaxWaves][2];
   uint32_t bcast[4];
 };
+
+// u32 image of an fp32 bit pattern, monotone in the value, with -0 and +0 on
+// one key: x >= +0 -> bits + 2^31, x < 0 -> -bits (mod 2^32).  Never 0.
+__device__ __forceinline__ uint32_t value_key(uint32_t u) {
+  const uint32_t s = (uint32_t)((int32_t)u >> 31);
+  uint32_t c;   // s ? 1 : 2^31, one bitfield insert (the compiler's own form takes three)
+  asm("v_bfi_b32 %0, %1, 1, %2" : "=v"(c) : "v"(s), "s"(0x80000000u));
+  return (u ^ s) + c;
+}
 
 // Wave-wide reductions and scans on DPP and permlane moves (VALU only; the
 // shuffle forms go through LDS with a round trip per step).
@@ -123,18 +148,15 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// element e of a row as fp32 (exact for bf16)
-template <bool BF16>
-__device__ __forceinline__ float elem(const void* Xr, int64_t e) {
-  if (BF16) return __uint_as_float((uint32_t)static_cast<const uint16_t*>(Xr)[e] << 16);
-  return static_cast<const float*>(Xr)[e];
-}
-
-// 4 consecutive values starting at element i (i % 4 == 0) of the row.
-template <int MODE, bool VEC, bool BF16>
+// Bit patterns (as fp32) of the 4 consecutive values starting at element i
+// (i % 4 == 0) of the row; CHECK: slots at or past n read as 0 and are
+// flagged in `ok`.
+template <int MODE, bool VEC, bool BF16, bool CHECK>
 __device__ __forceinline__ void load4(const TopkArgs& a, const void* Xr, const int32_t* blk, int i,
-                                      int n, float (&v)[4]) {
-  if (VEC && i + 3 < n) {
+                                      int n, uint32_t (&u)[4], bool (&ok)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ok[e] = !CHECK || i + e < n;
+  if (VEC && (!CHECK || i + 3 < n)) {
     int64_t p = i;
     if (MODE == MODE_GATHER) {
       p = (int64_t)blk[i >> 3] * kBlock + (i & 7);
@@ -142,27 +164,26 @@ __device__ __forceinline__ void load4(const TopkArgs& a, const void* Xr, const i
     }
     if (BF16) {
       const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Xr) + p);
-      v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
-      v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+      u[0] = x.x << 16; u[1] = x.x & 0xffff0000u; u[2] = x.y << 16; u[3] = x.y & 0xffff0000u;
     } else {
-      const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(Xr) + p);
-      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const float*>(Xr) + p);
+      u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
     }
     return;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int ie = i + e;
-    float x = 0.f;
-    if (ie < n) {
+    uint32_t x = 0u;
+    if (ok[e]) {
       int64_t p = ie;
       if (MODE == MODE_GATHER) {
         p = (int64_t)blk[ie >> 3] * kBlock + (ie & 7);
         if (p < 0 || p >= a.ld) p = 0;
       }
-      x = elem<BF16>(Xr, p);
+      x = BF16 ? (uint32_t)static_cast<const uint16_t*>(Xr)[p] << 16 : static_cast<const uint32_t*>(Xr)[p];
     }
-    v[e] = x;
+    u[e] = x;
   }
 }
 
@@ -173,9 +194,10 @@ __device__ __forceinline__ int32_t map_index(const int32_t* blk, int i) {
 }
 
 // Select the bin holding the rem-th largest of hist[0..kBins) (counted from
-// the top).  Returns the bin and, in *above, the count of the bins above it.
-template <int THREADS>
-__device__ __forceinline__ int find_bin(TopkShared& sh, uint32_t rem, uint32_t* above_out) {
+// the top).  Returns the bin; *above gets the count of the bins above it and
+// *count the bin's own count.
+template <int THREADS, class Sh>
+__device__ __forceinline__ int find_bin(Sh& sh, uint32_t rem, uint32_t* above_out, uint32_t* count_out) {
   constexpr int W = THREADS / 64;
   constexpr int BPT = kBins / THREADS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -200,6 +222,7 @@ __device__ __forceinline__ int find_bin(TopkShared& sh, uint32_t rem, uint32_t* 
       if (acc < rem && rem <= acc + cb[q]) {
         sh.bcast[0] = (uint32_t)(kBins - 1 - BPT * tid - q);
         sh.bcast[1] = acc;
+        sh.bcast[3] = cb[q];
       }
       acc += cb[q];
     }
@@ -207,16 +230,20 @@ __device__ __forceinline__ int find_bin(TopkShared& sh, uint32_t rem, uint32_t* 
   __syncthreads();
   const int b = (int)sh.bcast[0];
   *above_out = sh.bcast[1];
+  *count_out = sh.bcast[3];
   __syncthreads();
   return b;
 }
 
-// RESIDENT: every row fits one chunk (n <= THREADS * 64), loaded once.
+// RESIDENT: every row fits one chunk (n <= THREADS * 32), loaded once.
 template <int MODE, bool VEC, int THREADS, bool RESIDENT, bool BF16>
-__global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDENT ? 4 : THREADS == 1024 ? 8 : THREADS == 512 ? 6 : 4))) void topk_kernel(TopkArgs a) {
   constexpr int W = THREADS / 64;
   constexpr int kChunk = W * kWaveSlice;
-  __shared__ TopkShared sh;
+  constexpr bool kMapped = MODE == MODE_BLOCKMAP || MODE == MODE_GATHER;
+  using Sh = TopkShared<THREADS>;
+  constexpr int kList = Sh::kList;
+  __shared__ Sh sh;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,14 +255,14 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
   } else {
     n = a.nvalid[row];
     if (n < 0) n = 0;
-    if ((MODE == MODE_BLOCKMAP || MODE == MODE_GATHER) && n > a.kb * kBlock) n = a.kb * kBlock;
+    if (kMapped && n > a.kb * kBlock) n = a.kb * kBlock;
   }
   if (MODE != MODE_GATHER && (int64_t)n > a.ld) n = (int)a.ld;   // never read past the row
   const int k = a.k;
   int32_t* out = a.out + (int64_t)row * k;
   const int32_t pad = MODE == MODE_KEYS ? 0x7fffffff : -1;
   const int32_t off = (MODE != MODE_KEYS && a.pos_offset) ? a.pos_offset[row] : 0;
-  const int32_t* blk = (MODE == MODE_BLOCKMAP || MODE == MODE_GATHER) ? a.blocks + (int64_t)row * a.kb : nullptr;
+  const int32_t* blk = kMapped ? a.blocks + (int64_t)row * a.kb : nullptr;
   const void* Xr = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(a.X) + (int64_t)row * a.ld)
                         : static_cast<const void*>(static_cast<const float*>(a.X) + (int64_t)row * a.ld);
 
@@ -247,52 +274,68 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
 
   const int nchunks = RESIDENT ? 1 : (n + kChunk - 1) / kChunk;
   uint32_t key[kTopkSteps][4];
-  int32_t bid[kTopkSteps];   // block id of step j's elements (modes 1, 2)
   // element index of key[j][e] in chunk c: c * kChunk + ebase + 256 j + e
   const int ebase = wave * kWaveSlice + 4 * lane;
   auto load_chunk = [&](int c) {
+    if ((c + 1) * kChunk <= n) {   // the whole chunk is inside the row
 #pragma unroll
-    for (int j = 0; j < kTopkSteps; ++j) {
-      const int i = c * kChunk + ebase + 256 * j;
-      if (MODE == MODE_BLOCKMAP || MODE == MODE_GATHER) bid[j] = i < n ? blk[i >> 3] : 0;
-      float v[4];
-      load4<MODE, VEC, BF16>(a, Xr, blk, i, n, v);
+      for (int j = 0; j < kTopkSteps; ++j) {
+        const int i = c * kChunk + ebase + 256 * j;
+        uint32_t u[4];
+        bool ok[4];
+        load4<MODE, VEC, BF16, false>(a, Xr, blk, i, n, u, ok);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) key[j][e] = i + e < n ? order_key(v[e]) : 0u;
+        for (int e = 0; e < 4; ++e) key[j][e] = value_key(u[e]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kTopkSteps; ++j) {
+        const int i = c * kChunk + ebase + 256 * j;
+        uint32_t u[4];
+        bool ok[4];
+        load4<MODE, VEC, BF16, true>(a, Xr, blk, i, n, u, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[j][e] = ok[e] ? value_key(u[e]) : 0u;
+      }
     }
   };
   if (nchunks == 1) load_chunk(0);
 
   // ---- 1a. finite extremes of the row ----
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  // y = key + 2^23 sends +inf to 0 (below every finite key); z = key - 2^23 - 1
+  // sends -inf, the empty slots and +inf above every finite key, so plain
+  // max / min ignore the non-finite keys
+  uint32_t ymax = 0u, zmin = 0xffffffffu;
   for (int c = 0; c < nchunks; ++c) {
     if (nchunks > 1) load_chunk(c);
 #pragma unroll
     for (int j = 0; j < kTopkSteps; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t x = key[j][e];
-        const bool fin = x > kNegInf && x < kPosInf;
-        kmin = min(kmin, fin ? x : 0xffffffffu);
-        kmax = max(kmax, fin ? x : 0u);
+        ymax = max(ymax, key[j][e] + 0x00800000u);
+        zmin = min(zmin, key[j][e] - 0x00800001u);
       }
   }
-  kmin = wave_min(kmin);
-  kmax = wave_max(kmax);
+  ymax = wave_max(ymax);
+  zmin = wave_min(zmin);
   if (lane == 0) {
-    sh.wred[wave][0] = kmin;
-    sh.wred[wave][1] = kmax;
+    sh.wred[wave][0] = zmin;
+    sh.wred[wave][1] = ymax;
   }
-  if (tid == 0) sh.bcast[2] = 0u;   // candidate list length
+  if (tid == 0) sh.bcast[2] = 0u;   // register path: candidate list length
   __syncthreads();
-  kmin = 0xffffffffu;
-  kmax = 0u;
+  zmin = 0xffffffffu;
+  ymax = 0u;
 #pragma unroll
   for (int w = 0; w < W; ++w) {
-    kmin = min(kmin, sh.wred[w][0]);
-    kmax = max(kmax, sh.wred[w][1]);
+    zmin = min(zmin, sh.wred[w][0]);
+    ymax = max(ymax, sh.wred[w][1]);
   }
-  if (kmin > kmax) kmin = kmax = 0x80000000u;   // no finite key: any finite stand-in
+  uint32_t kmin = 0x80000000u, kmax = 0x80000000u;   // no finite key: any finite stand-in
+  if (zmin <= 0xfefffffeu) {
+    kmin = zmin + 0x00800001u;
+    kmax = ymax - 0x00800000u;
+  }
   kmin = __builtin_amdgcn_readfirstlane(kmin);
   kmax = __builtin_amdgcn_readfirstlane(kmax);
   const uint32_t span = kmax - kmin;
@@ -302,10 +345,11 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
   // digit: -inf and the empty slots -> 0, finite x -> 1 + ((x - kmin) >> shift),
   // +inf -> one above the largest finite digit; monotone in x
   const uint32_t lo = kmin - (1u << shift), hi = kmax + (1u << shift);
+  const uint32_t top = hi - lo;
   auto digit0 = [&](uint32_t x) -> uint32_t {
-    return (min(max(x, lo), hi) - lo) >> shift;
+    return min(__builtin_elementwise_sub_sat(x, lo), top) >> shift;
   };
-  const uint32_t inf_digit = (hi - lo) >> shift;
+  const uint32_t inf_digit = top >> shift;
 
   // ---- 1b. pass 0: histogram of the digits ----
   for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
@@ -318,10 +362,11 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
       for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[digit0(key[j][e])], 1u);
   }
   __syncthreads();
-  uint32_t above;
-  const uint32_t bin = (uint32_t)find_bin<THREADS>(sh, (uint32_t)k, &above);
+  uint32_t above, bin_count;
+  const uint32_t bin = (uint32_t)find_bin<THREADS>(sh, (uint32_t)k, &above, &bin_count);
   uint32_t need = (uint32_t)k - above;
-  uint32_t K;
+  bool known = true;
+  uint32_t K = 0u;
   if (bin == 0u) {
     K = kNegInf;
   } else if (bin >= inf_digit) {
@@ -329,12 +374,125 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
   } else if (shift == 0) {
     K = kmin + (bin - 1u);
   } else {
-    // ---- 1c. the chosen bin's keys: refine their low `shift` bits ----
+    known = false;
+  }
+  // every kept key is >= floor_key; above + bin_count elements reach it (an
+  // upper bound in the -inf bin, which also counts the empty slots)
+  const uint32_t floor_key = known ? K : lo + (bin << shift);
+
+  if (above + bin_count <= (uint32_t)kList) {
+    // ---- 2. list of the elements >= floor_key, in index order ----
+    uint32_t m = 0u;
+    for (int c = 0; c < nchunks; ++c) {
+      if (nchunks > 1) load_chunk(c);
+      uint32_t wn = 0u;
+#pragma unroll
+      for (int j = 0; j < kTopkSteps; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wn += (uint32_t)__popcll(__ballot(key[j][e] >= floor_key));
+      if (lane == 0) sh.wcnt[wave][0] = wn;
+      __syncthreads();
+      uint32_t p = m, tot = 0u;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const uint32_t v = sh.wcnt[w][0];
+        p += w < wave ? v : 0u;
+        tot += v;
+      }
+      // an opaque copy of the bound keeps the counting ballots above from
+      // being reused (and all held live) here
+      uint32_t F = __builtin_amdgcn_readfirstlane(floor_key);
+      asm volatile("" : "+s"(F));
+#pragma unroll
+      for (int j = 0; j < kTopkSteps; ++j) {
+        uint64_t G[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) G[e] = __ballot(key[j][e] >= F);
+        if ((G[0] | G[1] | G[2] | G[3]) != 0u) {
+          uint32_t q = p;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q += lanes_below(G[e]);
+          const int ib = c * kChunk + ebase + 256 * j;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (key[j][e] >= F) {
+              if (q < (uint32_t)kList)
+                *reinterpret_cast<uint2*>(&sh.list[2 * q]) = make_uint2((uint32_t)(ib + e), key[j][e]);
+              ++q;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p += (uint32_t)__popcll(G[e]);
+        }
+      }
+      m += tot;
+      __syncthreads();
+    }
+    m = min(m, (uint32_t)kList);
+
+    // ---- 3a. the bin's entries: refine the low `shift` bits of K ----
+    if (!known) {
+      uint32_t fixed = (bin - 1u) << shift;   // known bits of (K - kmin)
+      int low = shift;                        // bits below `low` still unknown
+      while (low > 0) {
+        const int width = low < 11 ? low : 11;
+        const int sh_lo = low - width;
+        const uint32_t hi_mask = ~((1u << low) - 1u);
+        for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < m; i += THREADS) {
+          const uint32_t r = sh.list[2 * i + 1] - kmin;
+          if ((r & hi_mask) == fixed) atomicAdd(&sh.hist[(r >> sh_lo) & ((1u << width) - 1u)], 1u);
+        }
+        __syncthreads();
+        uint32_t ab, cnt;
+        const uint32_t d = (uint32_t)find_bin<THREADS>(sh, need, &ab, &cnt);
+        need -= ab;
+        fixed |= d << sh_lo;
+        low = sh_lo;
+      }
+      K = kmin + fixed;
+    }
+
+    // ---- 3b. ordered output from the list ----
+    // thread t takes entries [t E, t E + E); one scan of the packed
+    // (greater << 16 | equal) counts gives every entry its output slot
+    const uint32_t E = (m + THREADS - 1) / THREADS;
+    const uint32_t s0 = min((uint32_t)tid * E, m), s1 = min(s0 + E, m);
+    uint32_t cnt = 0u;
+    for (uint32_t i = s0; i < s1; ++i) {
+      const uint32_t x = sh.list[2 * i + 1];
+      cnt += x > K ? 0x10000u : (x == K ? 1u : 0u);
+    }
+    const uint32_t x = wave_incl_scan(cnt);
+    if (lane == 63) sh.wcnt[wave][1] = x;
+    __syncthreads();
+    uint32_t before = 0u;
+#pragma unroll
+    for (int w = 0; w < W; ++w) before += w < wave ? sh.wcnt[w][1] : 0u;
+    const uint32_t excl = before + x - cnt;
+    uint32_t gpre = excl >> 16, qpre = excl & 0xffffu;
+    for (uint32_t i = s0; i < s1; ++i) {
+      const uint2 ent = *reinterpret_cast<const uint2*>(&sh.list[2 * i]);
+      const bool g = ent.y > K, q = ent.y == K;
+      if (g || (q && qpre < need)) out[gpre + min(qpre, need)] = map_index<MODE>(blk, (int)ent.x) + off;
+      gpre += g ? 1u : 0u;
+      qpre += q ? 1u : 0u;
+    }
+    if (MODE == MODE_KEYS && tid == 0) a.n_kept[row] = k;
+    return;
+  }
+
+  // ==== register path: the list would not fit ====
+  if (!known) {
+    // ---- the chosen bin's keys: refine their low `shift` bits ----
     // (an opaque copy of the digit bounds keeps the compiler from holding
     // every element's digit from pass 0 in registers until here)
-    uint32_t lo_c = __builtin_amdgcn_readfirstlane(lo), hi_c = __builtin_amdgcn_readfirstlane(hi);
-    asm volatile("" : "+s"(lo_c), "+s"(hi_c));
-    auto digit0c = [&](uint32_t x) -> uint32_t { return (min(max(x, lo_c), hi_c) - lo_c) >> shift; };
+    uint32_t lo_c = __builtin_amdgcn_readfirstlane(lo), top_c = __builtin_amdgcn_readfirstlane(top);
+    asm volatile("" : "+s"(lo_c), "+s"(top_c));
+    auto digit0c = [&](uint32_t x) -> uint32_t {
+      return min(__builtin_elementwise_sub_sat(x, lo_c), top_c) >> shift;
+    };
     for (int c = 0; c < nchunks; ++c) {
       if (nchunks > 1) load_chunk(c);
       // per-lane hit count, one LDS atomic per wave, then in-order slots
@@ -378,6 +536,10 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
           if ((r & hi_mask) == fixed) atomicAdd(&sh.hist[(r >> sh_lo) & ((1u << width) - 1u)], 1u);
         }
       } else {
+        // (an opaque copy of kmin keeps key - kmin from being hoisted out of
+        // the refine loop: 32 more live registers)
+        uint32_t kmin_c = kmin;
+        asm volatile("" : "+s"(kmin_c));
         for (int c = 0; c < nchunks; ++c) {
           if (nchunks > 1) load_chunk(c);
 #pragma unroll
@@ -385,15 +547,15 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t x = key[j][e];
-              const uint32_t r = x - kmin;
+              const uint32_t r = x - kmin_c;
               if (digit0c(x) == bin && (r & hi_mask) == fixed)
                 atomicAdd(&sh.hist[(r >> sh_lo) & ((1u << width) - 1u)], 1u);
             }
         }
       }
       __syncthreads();
-      uint32_t ab;
-      const uint32_t d = (uint32_t)find_bin<THREADS>(sh, need, &ab);
+      uint32_t ab, cnt;
+      const uint32_t d = (uint32_t)find_bin<THREADS>(sh, need, &ab, &cnt);
       need -= ab;
       fixed |= d << sh_lo;
       low = sh_lo;
@@ -401,7 +563,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
     K = kmin + fixed;
   }
 
-  // ---- 2. ordered compaction ----
+  // ---- ordered compaction over the registers ----
   uint32_t gt_run = 0u, eq_run = 0u;   // block-wide, over previous chunks
   for (int c = 0; c < nchunks; ++c) {
     if (nchunks > 1) load_chunk(c);
@@ -453,9 +615,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(TopkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool g = key[j][e] > Kc, q = key[j][e] == Kc;
-          const int32_t pos = (MODE == MODE_BLOCKMAP || MODE == MODE_GATHER)
-                                  ? bid[j] * kBlock + ((ib + e) & 7) : ib + e;
-          if (g || (q && qpre < need)) out[gpre + min(qpre, need)] = pos + off;
+          if (g || (q && qpre < need)) out[gpre + min(qpre, need)] = map_index<MODE>(blk, ib + e) + off;
           gpre += g ? 1u : 0u;
           qpre += q ? 1u : 0u;
         }

@@ -313,6 +313,44 @@ def random_matrix(seed: int, rows: int, width: int, ties: bool = True,
     return x
 
 
+def crowded_rows(seed: int, kind: str, rows: int, width: int, k: int, cluster: int = 0) -> np.ndarray:
+    """float32 [rows, width] whose k-th largest value sits where many values
+    crowd together, positions shuffled per row.  kind:
+      'constant'  every value 3.0;
+      'zeros'     +0 and -0 only;
+      'cluster'   `cluster` values within a few thousand ulps above 1.0, in
+                  runs of three equal values, above ~N(-5, 0.3^2) filler, with
+                  two values at +1e30 and two at -1e30 widening the row's span;
+      'neginf'    k // 2 finite values ~ N(0, 8^2), the rest -inf;
+      'posinf'    k + k // 2 values +inf, the rest ~ N(0, 8^2);
+      'posinf_many'  a quarter of the row +inf, the rest ~ N(0, 8^2)."""
+    r = _rng(902, seed)
+    x = np.empty((rows, width), np.float32)
+    for i in range(rows):
+        if kind == "constant":
+            v = np.full(width, 3.0, np.float32)
+        elif kind == "zeros":
+            v = np.where(r.random(width) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        elif kind == "cluster":
+            c = min(cluster, width - 4)
+            ulp = np.float32(np.spacing(np.float32(1.0)))
+            clus = np.float32(1.0) + ulp * (np.arange(c) // 3).astype(np.float32)
+            fill = (r.standard_normal(width - 4 - c) * 0.3 - 5.0).astype(np.float32)
+            v = np.concatenate([np.float32([1e30, 1e30, -1e30, -1e30]), clus, fill]).astype(np.float32)
+        elif kind == "neginf":
+            v = np.full(width, -np.inf, np.float32)
+            nf = min(k // 2, width)
+            v[:nf] = r.standard_normal(nf) * 8.0
+        elif kind in ("posinf", "posinf_many"):
+            v = (r.standard_normal(width) * 8.0).astype(np.float32)
+            ni = min(width, k + k // 2 if kind == "posinf" else width // 4)
+            v[:ni] = np.inf
+        else:
+            raise ValueError(kind)
+        x[i] = v[r.permutation(width)]
+    return x
+
+
 def to_bf16(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Input construction for bf16 operands: float32 -> (bf16 bit patterns as
     uint16, the same values as float32), nearest with ties to even."""
