@@ -23,8 +23,10 @@ constexpr int kSparseWaves = 4;
 // kSparseTargetWaves waves run: up to 8 consecutive units per wave on big
 // tables (8 and 32 measured alike on MI355X, 1 was 8% slower: the query
 // reload and the wave launch per 512 columns), or a unit split over 2, 4 or
-// 8 waves (8 / split groups each) when there are few rows, as in decode.
-constexpr int kSparseTargetWaves = 8192;
+// 8 waves (8 / split groups each) when there are fewer units than that.  On
+// 64 decode rows (2048 units) one unit per wave ran in 16 us against 26 us
+// split over 4 waves: each wave's query and block-id loads are fixed latency.
+constexpr int kSparseTargetWaves = 2048;
 constexpr int kMaxUnitsPerWave = 8;
 
 // K operands of 4 tiles (8 candidate blocks) of one unit.
