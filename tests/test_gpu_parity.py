@@ -301,7 +301,7 @@ def test_dense_keys_fused(idx, name, skip):
 # idx_topk_blocks (bit-exact)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kb,maxblk", [(16, 128), (2048, 32768), (2048, 8192), (3, 40)])
+@pytest.mark.parametrize("kb,maxblk", [(16, 128), (2048, 32768), (2048, 8192), (3, 40), (64, 8192)])
 def test_topk_blocks_bitexact(idx, kb, maxblk):
     rows = 48
     keys = workloads.random_matrix(kb + maxblk, rows, maxblk)
@@ -325,7 +325,7 @@ def test_topk_blocks_bitexact(idx, kb, maxblk):
 # idx_topk_rows (bit-exact, three column modes)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("width,k", [(16384, 512), (1024, 32), (70000, 512), (300, 512)])
+@pytest.mark.parametrize("width,k", [(16384, 512), (1024, 32), (70000, 512), (300, 512), (9000, 7)])
 def test_topk_rows_identity(idx, width, k):
     rows = 32
     X = workloads.random_matrix(7 * width + k, rows, width)
@@ -351,7 +351,7 @@ def _random_blocks(seed, rows, kb, nblk_max):
     return blocks, nk
 
 
-@pytest.mark.parametrize("kb,k", [(2048, 512), (16, 32), (64, 8)])
+@pytest.mark.parametrize("kb,k", [(2048, 512), (16, 32), (64, 8), (1024, 100)])
 def test_topk_rows_blockmap_and_gather(idx, kb, k):
     rows = 24
     nblk_max = 4 * kb + 5
