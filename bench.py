@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "tiny"])
     ap.add_argument("--cpu-rows", type=int, default=192,
                     help="rows of the CPU oracle sample (0 = skip the CPU baseline)")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="time replays of the step captured as one HIP graph (auto: on for "
+                         "tables of at most 256 rows, whose steps are bound by per-call host cost)")
     ap.add_argument("--consumer-bf16", action="store_true",
                     help="the bf16 consumer-score variant (scores and their top-k in bf16)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -196,17 +199,30 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {args.warmup} warmup steps done", file=sys.stderr, flush=True)
 
-    rec = Recorder()
-    ch.recorder = rec
+    use_graph = args.graph == "on" or (args.graph == "auto" and wl.rows <= Chunk.OVERLAP_MAX_ROWS)
+    if use_graph:
+        ch.capture()
+        for i in range(args.warmup):
+            ch.replay()
+    step = ch.replay if use_graph else ch.run
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ch.run()
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ch.recorder = None
     ms = (t1 - t0) * 1000.0 / args.steps
     print(f"[bench] {args.steps} timed steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-call times from events at each call's start and end, in extra steps
+    # after the timed ones (recording ~25 events per step costs host time that
+    # would otherwise be charged to small configs' steps)
+    rec = Recorder()
+    ch.recorder = rec
+    for i in range(min(args.steps, 5)):
+        ch.run()
+    torch.cuda.synchronize()
+    ch.recorder = None
 
     work = algorithmic_work(wl, score_bytes=2 if args.consumer_bf16 else 4)
     ncons = len(ch.cons_top)
@@ -221,7 +237,7 @@ def main():
     t_exp = avg("topk_blocks>", "expand>")
     t_src = avg("source_topk<", "source_topk>")
     t_sp = [avg(f"sparse{i}<", f"sparse{i}>") for i in range(ncons)]
-    t_tr = [avg(f"sparse{i}>", f"topk_rows{i}>") for i in range(ncons)]
+    t_tr = [avg(f"topk_rows{i}<", f"topk_rows{i}>") for i in range(ncons)]
     dense_tflops = work["dense_flops"] / (t_dense * 1e-3) / 1e12
     dense_name = "score_dense_keys" if ch.fused_keys else "score_dense"
     kernels = {
@@ -255,7 +271,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "rows": wl.rows, "heads": wl.heads, "kb": wl.kb,
                    "topk": wl.kc, "consumers": ncons,
-                   "consumer_scores": "bf16" if args.consumer_bf16 else "fp32"},
+                   "consumer_scores": "bf16" if args.consumer_bf16 else "fp32",
+                   "step": "one HIP graph replay" if use_graph else "eager calls"},
         "roofline": {"bound": "mfma", "kernel": dense_name,
                      "achieved": round(dense_tflops, 2), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dense_tflops / PEAK_FP4_TFLOPS, 4),

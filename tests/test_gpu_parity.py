@@ -651,6 +651,62 @@ def test_chunk_decode(idx):
     _check_chunk(wl, ch, np.arange(0, 64, 4), None)
 
 
+def test_chunk_decode_overlap_matches_serial(idx):
+    """Few rows run the selects on their own stream, behind the next consumer's
+    scores, with two score buffers reused across 4 consumers; the outputs are
+    those of the serial order bit for bit (the serial order is checked against
+    the oracle above)."""
+    from two_level_top_amd.chunk import Chunk
+    wl = workloads.decode()
+    say("chunk decode, 4 consumers: overlapped selects vs serial")
+    a = Chunk(wl, overlap_selects=True)
+    b = Chunk(wl, overlap_selects=False)
+    assert a.overlap and not b.overlap and len(a.T) == 2 and len(a.cons_top) == 4
+    for _ in range(2):
+        a.run()
+        b.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(a.src_top), host(b.src_top))
+    for x, y in zip(a.cons_top, b.cons_top):
+        assert np.array_equal(host(x), host(y))
+    for name in ("blocks", "n_kept", "phys", "valid_len"):
+        assert np.array_equal(host(getattr(a.table, name)), host(getattr(b.table, name))), name
+
+
+def test_chunk_graph_replay(idx):
+    """The decode step captured as one HIP graph: every replay reproduces the
+    eager step's outputs bit for bit, with eager work between the replays
+    (every output buffer overwritten first, so a replay that skipped a call
+    would show)."""
+    from two_level_top_amd.chunk import Chunk
+    wl = workloads.decode()
+    say("chunk decode captured as a HIP graph, 3 replays")
+    ch = Chunk(wl)
+    ch.run()
+    torch.cuda.synchronize()
+    names = ("blocks", "n_kept", "phys", "valid_len")
+    ref = {"S": host(ch.S), "src": host(ch.src_top), **{n: host(getattr(ch.table, n)) for n in names}}
+    ref_c = [host(t) for t in ch.cons_top]
+    ch.capture()
+    for _ in range(3):
+        ch.S.fill_(float("nan"))
+        ch.src_top.fill_(-7)
+        for t in ch.cons_top:
+            t.fill_(-7)
+        for n in names:
+            getattr(ch.table, n).fill_(-7)
+        torch.cuda.synchronize()
+        ch.replay()
+        torch.cuda.synchronize()
+        valid = np.arange(wl.ld)[None, :] < wl.lens[:, None]   # S past len is never written
+        assert np.array_equal(host(ch.S)[valid], ref["S"][valid])
+        assert np.array_equal(host(ch.src_top), ref["src"])
+        for t, r in zip(ch.cons_top, ref_c):
+            assert np.array_equal(host(t), r)
+        for n in names:
+            assert np.array_equal(host(getattr(ch.table, n)), ref[n]), n
+
+
 def test_chunk_mixed_small(idx):
     wl = workloads.mixed(n_consumers=1, decode_rows=32, max_decode_ctx=65536)
     say(f"chunk mixed (rows {wl.rows})")
