@@ -23,12 +23,16 @@
 namespace idxk {
 
 // Register-resident query of one row: HB blocks of 16 heads plus the folded
-// block.
+// block.  The ue8m0 scales of the blocks share one register (byte hb, picked
+// by the MFMA's scale byte select), and the row's half weights share one
+// register too: lane 16 g + 4 hb + v holds the weight of head 16 hb + 4 g + v,
+// which every lane of row g (the 16 lanes that receive heads 4 g .. 4 g + 3 of
+// each block) reads with a DPP row broadcast inside its FMA.
 template <int HB>
 struct RowFrag {
   uint4 a[HB];      // A operand: 32 e2m1 codes of head (l % 16), group (l / 16)
-  int sa[HB];       // that group's ue8m0 scale
-  float w[HB][4];   // half the weights of the heads 4 * (l / 16) + v of each block
+  int sa;           // byte hb: that group's ue8m0 scale in block hb
+  float w;          // half weights, laid out as above
   uint4 at;         // folded query: term (l % 16), group (l / 16)
   int st;
 };
@@ -37,26 +41,65 @@ template <int HB>
 __device__ __forceinline__ void load_row(const QueryArgs& q, const uint8_t* fold, int r, int lane,
                                          RowFrag<HB>& f) {
   const int g = lane >> 4;
+  f.sa = 0;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int h = hb * 16 + (lane & 15);
+    int sc = 127;
     if (h < q.heads) {
       const size_t base = (size_t)r * q.heads + h;
       f.a[hb] = *reinterpret_cast<const uint4*>(q.vals + base * kValBytes + g * 16);
-      f.sa[hb] = q.scales[base * kScaleBytes + g];
+      sc = q.scales[base * kScaleBytes + g];
     } else {
       f.a[hb] = make_uint4(0u, 0u, 0u, 0u);
-      f.sa[hb] = 127;
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int hw = hb * 16 + 4 * g + v;
-      f.w[hb][v] = hw < q.heads ? 0.5f * q.w[(size_t)r * q.heads + hw] : 0.f;
-    }
+    f.sa |= sc << (8 * hb);
+  }
+  {
+    const int m = lane & 15;   // 4 hb + v
+    const int hw = 16 * (m >> 2) + 4 * g + (m & 3);
+    f.w = (m >> 2) < HB && hw < q.heads ? 0.5f * q.w[(size_t)r * q.heads + hw] : 0.f;
+    asm volatile("s_nop 1" : "+v"(f.w));   // VALU write -> DPP read of f.w
   }
   const uint8_t* fr = fold + (size_t)r * kFoldRowBytes;
   f.at = *reinterpret_cast<const uint4*>(fr + (lane & 15) * kValBytes + g * 16);
   f.st = fr[kFoldTerms * kValBytes + (lane & 15) * kScaleBytes + g];
+}
+
+// MFMA of query block HBI (scale byte HBI of the packed scales)
+template <int HB, int HBI>
+__device__ __forceinline__ v4f block_mfma(const RowFrag<HB>& f, uint4 b, int sb) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v8i av = {(int)f.a[HBI].x, (int)f.a[HBI].y, (int)f.a[HBI].z, (int)f.a[HBI].w, 0, 0, 0, 0};
+  v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, zero, 4, 4, HBI, f.sa, 0, sb);
+}
+
+// s += (the half weight in lane M of this lane's 16-lane row) * |x|
+template <int M>
+__device__ __forceinline__ void fma_bcast_abs(float& s, float w, float x) {
+  asm("v_fmac_f32_dpp %0, %1, |%2| row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(s) : "v"(w), "v"(x), "i"(M));
+}
+
+template <int HB, int HBI = 0>
+__device__ __forceinline__ void tile_mfma_blocks(const RowFrag<HB>& f, uint4 b, int sb, v4f (&acc)[HB + 1]) {
+  if constexpr (HBI < HB) {
+    acc[HBI + 1] = block_mfma<HB, HBI>(f, b, sb);
+    tile_mfma_blocks<HB, HBI + 1>(f, b, sb, acc);
+  }
+}
+
+template <int HB, int HBI = 0>
+__device__ __forceinline__ void epilogue_blocks(float& s0, float& s1, float& s2, float& s3, float w,
+                                                const v4f (&acc)[HB + 1]) {
+  if constexpr (HBI < HB) {
+    fma_bcast_abs<4 * HBI + 0>(s0, w, acc[HBI + 1][0]);
+    fma_bcast_abs<4 * HBI + 1>(s1, w, acc[HBI + 1][1]);
+    fma_bcast_abs<4 * HBI + 2>(s2, w, acc[HBI + 1][2]);
+    fma_bcast_abs<4 * HBI + 3>(s3, w, acc[HBI + 1][3]);
+    epilogue_blocks<HB, HBI + 1>(s0, s1, s2, s3, w, acc);
+  }
 }
 
 // The HB + 1 MFMAs of one tile (folded block first) ...
@@ -64,39 +107,37 @@ template <int HB>
 __device__ __forceinline__ void tile_mfma(const RowFrag<HB>& f, uint4 b, int sb, v4f (&acc)[HB + 1]) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   acc[0] = mfma_fp4_16x16x128(f.at, b, f.st, sb, zero);
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) acc[hb + 1] = mfma_fp4_16x16x128(f.a[hb], b, f.sa[hb], sb, zero);
+  tile_mfma_blocks<HB>(f, b, sb, acc);
 }
 
 // ... and their epilogue: this lane's share of the score for its tile column,
 // the folded block's 4 terms plus 4 * HB heads, in four independent chains.
+// The FMAs below are inline assembly, which the compiler's hazard tracking
+// does not see into: this passes the tile's MFMA results through one asm
+// statement that waits out the MFMA-result-to-VALU wait states itself (12;
+// the compiler itself keeps 8 between this MFMA and a VALU read of its
+// result).
 template <int HB>
-__device__ __forceinline__ float tile_epilogue(const RowFrag<HB>& f, const v4f (&acc)[HB + 1]) {
-  float s0 = acc[0][0], s1 = acc[0][1], s2 = acc[0][2], s3 = acc[0][3];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    s0 = fmaf(f.w[hb][0], fabsf(acc[hb + 1][0]), s0);
-    s1 = fmaf(f.w[hb][1], fabsf(acc[hb + 1][1]), s1);
-    s2 = fmaf(f.w[hb][2], fabsf(acc[hb + 1][2]), s2);
-    s3 = fmaf(f.w[hb][3], fabsf(acc[hb + 1][3]), s3);
-  }
-  return (s0 + s1) + (s2 + s3);
+__device__ __forceinline__ void settle(v4f (&acc)[HB + 1]) {
+  if constexpr (HB == 1)
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[0]), "+v"(acc[1]));
+  else if constexpr (HB == 2)
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]));
+  else if constexpr (HB == 3)
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 3"
+                 : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]));
 }
 
-// This lane's share of the score for its tile column (one tile, one row).
 template <int HB>
-__device__ __forceinline__ float tile_partial(const RowFrag<HB>& f, uint4 b, int sb) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const v4f lin = mfma_fp4_16x16x128(f.at, b, f.st, sb, zero);
-  float s0 = lin[0], s1 = lin[1], s2 = lin[2], s3 = lin[3];
+__device__ __forceinline__ float tile_epilogue(const RowFrag<HB>& f, const v4f (&acc_in)[HB + 1]) {
+  v4f acc[HB + 1];
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const v4f acc = mfma_fp4_16x16x128(f.a[hb], b, f.sa[hb], sb, zero);
-    s0 = fmaf(f.w[hb][0], fabsf(acc[0]), s0);
-    s1 = fmaf(f.w[hb][1], fabsf(acc[1]), s1);
-    s2 = fmaf(f.w[hb][2], fabsf(acc[2]), s2);
-    s3 = fmaf(f.w[hb][3], fabsf(acc[3]), s3);
-  }
+  for (int i = 0; i <= HB; ++i) acc[i] = acc_in[i];
+  settle<HB>(acc);
+  float s0 = acc[0][0], s1 = acc[0][1], s2 = acc[0][2], s3 = acc[0][3];
+  epilogue_blocks<HB>(s0, s1, s2, s3, f.w, acc);
   return (s0 + s1) + (s2 + s3);
 }
 
