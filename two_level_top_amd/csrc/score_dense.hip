@@ -23,10 +23,13 @@
 // Rows of a wave that belong to different requests are scored one after
 // the other (their keys come from different pages).
 //
-// Measured on MI355X (long chunk): this 16x16x128 form at 3 waves per SIMD
-// beat a 32x32x64 form of the same epilogue (2 waves per SIMD at 249 VGPRs)
-// by about 12%, and issuing the next tile's MFMAs ahead of the epilogue or
-// deferring the stores past the next loads gained nothing.
+// Measured on MI355X (long chunk): this 16x16x128 form beat a 32x32x64 form
+// of the same epilogue (2 waves per SIMD at 249 VGPRs) by about 12%, and
+// issuing the next tile's MFMAs ahead of the epilogue or deferring the
+// stores past the next loads gained nothing.  With the weights and block
+// scales in one register each (score_common.h) and the two rows' tiles
+// scored one after the other, the kernel fits 124 VGPRs and runs 4 waves per
+// SIMD: 23.1 ms against 23.6 ms at 3 waves with both rows' MFMAs in flight.
 //
 // Fused block keys (the prefill PR's follow-up of folding the block amax into
 // the score kernel): after the 4-way reduction each lane holds one score of
@@ -113,11 +116,12 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* con
     float part[NR][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      v4f acc[NR][HB + 1];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) tile_mfma<HB>(f[r], cur.b[t], cur.sb[t], acc[r]);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) part[r][t] = tile_epilogue<HB>(f[r], acc[r]);
+      for (int r = 0; r < NR; ++r) {
+        v4f acc[HB + 1];
+        tile_mfma<HB>(f[r], cur.b[t], cur.sb[t], acc);
+        part[r][t] = tile_epilogue<HB>(f[r], acc);
+      }
     }
     const int p = c0 + i * kPage + lane;
 #pragma unroll
@@ -145,7 +149,7 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* con
 }
 
 template <int HB, bool KEYS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void score_dense_kernel(QueryArgs q, const uint8_t* __restrict__ fold,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_dense_kernel(QueryArgs q, const uint8_t* __restrict__ fold,
                                                           PoolArgs kp,
                                                           const int32_t* __restrict__ req,
                                                           const int32_t* __restrict__ len,
