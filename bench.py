@@ -136,6 +136,26 @@ def time_q_rope_quant(rows, heads, reps=20):
             "note": "query RoPE + MXFP4 quantisation before the chunk, timed apart from it"}
 
 
+def time_amax8(ch, bytes_per_call, reps=5):
+    """idx_amax8_varlen alone on the chunk's own score matrix (the chunk takes the
+    block keys from the fused dense pass instead), timed apart from the chunk."""
+    import torch
+    import two_level_top_amd as t
+    run = lambda: t.idx_amax8_varlen(ch.S, ch.rows.len, ch.keys, skip_le_blocks=ch.kb)
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = bytes_per_call / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "the unfused block-key pass over the chunk's S, timed apart from the chunk"}
+
+
 def cpu_baseline(wl, n_rows):
     """The oracle, as it stands, on n_rows evenly spaced rows of the same chunk."""
     import numpy as np
@@ -255,6 +275,10 @@ def main():
         "consumer_topk_rows": {"ms": round(float(np.mean(t_tr)), 4),
                                "GB/s": round(work["topk_rows_bytes"] / (np.mean(t_tr) * 1e-3) / 1e9, 1)},
     }
+    for name in ("topk_blocks", "consumer_topk_rows"):
+        kernels[name]["frac_hbm_peak"] = round(kernels[name]["GB/s"] / PEAK_HBM_GBS, 4)
+    if ch.fused_keys and wl.rows > Chunk.OVERLAP_MAX_ROWS:
+        kernels["amax8_varlen"] = time_amax8(ch, work["amax8_bytes"])
     kernels["q_rope_quant"] = time_q_rope_quant(wl.rows, wl.heads)
     out = {
         "metric": METRIC,

@@ -28,6 +28,10 @@ constexpr int kSparseWaves = 4;
 // split over 4 waves: each wave's query and block-id loads are fixed latency.
 constexpr int kSparseTargetWaves = 2048;
 constexpr int kMaxUnitsPerWave = 8;
+// scores are stored non-temporally (cache policy nt): a consumer's 1 GB of
+// scores is read once, by its top-k, after the whole table is scored
+// (measured 2.13 -> 2.10 ms per call on the long chunk)
+constexpr int kStoreNT = 2;
 
 // K operands of 4 tiles (8 candidate blocks) of one unit.
 struct GroupOps {
@@ -124,9 +128,9 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
       }
       const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
       if (BF16)
-        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(tot), trs, (uint32_t)(g * 64 + lane) * kEl, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(bf16_bits(tot), trs, (uint32_t)(g * 64 + lane) * kEl, 0, kStoreNT);
       else
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), trs, (uint32_t)(g * 64 + lane) * kEl, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), trs, (uint32_t)(g * 64 + lane) * kEl, 0, kStoreNT);
     };
     const int g0 = part * gper;
     const int g1 = min(ngroups, g0 + gper);
