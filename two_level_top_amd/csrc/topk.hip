@@ -166,7 +166,11 @@ __device__ __forceinline__ void load4(const TopkArgs& a, const void* Xr, const i
       const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(Xr) + p);
       u[0] = x.x << 16; u[1] = x.x & 0xffff0000u; u[2] = x.y << 16; u[3] = x.y & 0xffff0000u;
     } else {
-      const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const float*>(Xr) + p);
+      // non-temporal: every score or key is read once (block top-k 1.04 ->
+      // 1.01 ms, source top-k 0.73 -> 0.71 ms on the long chunk)
+      typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+      const u4v t = __builtin_nontemporal_load(reinterpret_cast<const u4v*>(static_cast<const float*>(Xr) + p));
+      const uint4 x = make_uint4(t[0], t[1], t[2], t[3]);
       u[0] = x.x; u[1] = x.y; u[2] = x.z; u[3] = x.w;
     }
     return;
