@@ -132,10 +132,14 @@ def test_dense_prefill_sampled(idx):
 
 @pytest.mark.parametrize("width,kb", [(2048, 16), (65536, 2048), (262144, 2048)])
 def test_amax8_bitexact(idx, width, kb):
-    rows = 64 if width <= 65536 else 24
+    rows = 64 if width <= 65536 else 32
     S = workloads.random_matrix(width, rows, width)
+    # lengths whose newest block falls at, just past or just before the
+    # boundaries of the kernel's 256-block wave slices and 1024-block workgroups
+    bounds = [8 * (kb + 256 * m) + d for m in (1, 2, 4, 5) for d in (-8, -7, 0, 1, 9)]
     lens = workloads.random_lengths(width, rows, 0, width,
-                                    extra=[0, 1, 7, 8, 9, width, width - 1, 8 * kb, 8 * kb + 1, 8 * kb - 1])
+                                    extra=[0, 1, 7, 8, 9, width, width - 1, 8 * kb, 8 * kb + 1, 8 * kb - 1]
+                                    + [b for b in bounds if b <= width])
     nblk = oracle.nblocks(lens)
     ldk = width // 8
     say(f"amax8 width={width} kb={kb}")
