@@ -20,22 +20,11 @@
 
 namespace idxk {
 
-__device__ __forceinline__ double e2m1_value(int code) {
-  const int m = code & 7;
-  const double mag = m < 4 ? 0.5 * m : (m == 4 ? 2.0 : (m == 5 ? 3.0 : (m == 6 ? 4.0 : 6.0)));
-  return (code & 8) ? -mag : mag;
-}
-
-// nearest e2m1 magnitude code of a in [0, 6] (ties to the even code)
+// nearest e2m1 magnitude code of a in [0, 6] (ties to the even code), as a
+// count of the grid midpoints below a (branch-free)
 __device__ __forceinline__ int e2m1_nearest(double a) {
-  if (a <= 0.25) return 0;
-  if (a < 0.75) return 1;
-  if (a <= 1.25) return 2;
-  if (a < 1.75) return 3;
-  if (a <= 2.5) return 4;
-  if (a < 3.5) return 5;
-  if (a <= 5.0) return 6;
-  return 7;
+  return (int)(a > 0.25) + (int)(a >= 0.75) + (int)(a > 1.25) + (int)(a >= 1.75) + (int)(a > 2.5) +
+         (int)(a >= 3.5) + (int)(a > 5.0);
 }
 
 template <int CTRL>
@@ -44,69 +33,78 @@ __device__ __forceinline__ double dpp_d(double v) {
   const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(v), CTRL, 0xf, 0xf, true);
   return __hiloint2double(hi, lo);
 }
-// max of lanes l and l ^ 16 (the swap returns, in every lane, the pair's
-// even-row value in [0] and its odd-row value in [1])
-__device__ __forceinline__ double max16_d(double v) {
-  const auto lo = __builtin_amdgcn_permlane16_swap(__double2loint(v), __double2loint(v), false, false);
-  const auto hi = __builtin_amdgcn_permlane16_swap(__double2hiint(v), __double2hiint(v), false, false);
-  return fmax(__hiloint2double((int)hi[0], (int)lo[0]), __hiloint2double((int)hi[1], (int)lo[1]));
-}
 
-// One query row per 128 lanes (two waves), lane d owning dimension d: the
-// 32 lanes of an aligned half-wave form one scale group, so a group's
-// largest residual is a 32-lane reduction and every step of the split runs
-// on all 128 dimensions at once.  The row's codes, scales and weights
-// (<= 4.6 KB) are first staged in LDS, so the head loop waits on one memory
-// latency rather than one per unrolled batch (few rows, as in decode, are
-// latency-bound).
-constexpr int kFoldRowsPerWG = 2;
+// One query row per wave, lane l owning dimensions 2 l and 2 l + 1 (the two
+// nibbles of code byte l of every head): the 16 lanes of a DPP row form one
+// scale group, so a group's largest residual is a 16-lane reduction and every
+// step of the split runs on all 128 dimensions at once.  The row's code bytes
+// are staged in LDS, together with the factor (w_h / 4) 2^(scale_hg - 127) of
+// every (head, group) and a table giving each code byte's two values as
+// 2 |e2m1| with its sign (hence the extra halving), so the head loop is two
+// LDS reads and one FMA per dimension.  The fp64 operations and their order are those of a plain
+// per-dimension loop over the heads.
+constexpr int kFoldRowsPerWG = 4;
 constexpr int kFoldMaxHeads = 64;
 
+// 2 * (value of e2m1 code c), as the fp64 the head sums multiply
+__device__ __forceinline__ double code_value2(int c) {
+  const int m2 = (0xC8643210u >> (4 * (c & 7))) & 15;   // 2 * |e2m1 value|
+  return (double)((c & 8) ? -m2 : m2);
+}
+
 __global__ __launch_bounds__(256) void fold_query_kernel(QueryArgs q, uint8_t* __restrict__ out) {
-  __shared__ uint4 stage[kFoldRowsPerWG][kFoldMaxHeads * (kValBytes + kScaleBytes + 4) / 16];
-  const int half = threadIdx.x >> 7;
-  const int row = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kFoldRowsPerWG + half));
+  __shared__ uint4 stage[kFoldRowsPerWG][kFoldMaxHeads * kValBytes / 16];
+  __shared__ double hscale[kFoldRowsPerWG][kFoldMaxHeads * 4];
+  __shared__ double2 pair[256];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int row = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kFoldRowsPerWG + wave));
   const bool live = row < q.rows;
-  const int rr = live ? row : q.rows - 1;   // a dead half computes a copy and stores nothing
-  const int d = threadIdx.x & 127;
-  const int g = d >> 5;
+  const int rr = live ? row : q.rows - 1;   // a dead wave computes a copy and stores nothing
   const int H = q.heads;
-  // stage: codes [H][64] (16-byte loads: vals is 16-byte aligned), then
-  // scales [H][4] and weights [H] (4-byte loads)
-  uint8_t* sb = reinterpret_cast<uint8_t*>(stage[half]);
-  const int vb = H * kValBytes, scb = H * kScaleBytes;
-  const uint4* src_v = reinterpret_cast<const uint4*>(q.vals + (size_t)rr * vb);
-  const uint32_t* src_s = reinterpret_cast<const uint32_t*>(q.scales + (size_t)rr * scb);
-  const uint32_t* src_w = reinterpret_cast<const uint32_t*>(q.w + (size_t)rr * H);
-  for (int i = d; i < vb / 16; i += 128) stage[half][i] = src_v[i];
-  uint32_t* s32 = reinterpret_cast<uint32_t*>(sb + vb);
-  if (d < H) {
-    s32[d] = src_s[d];
-    s32[H + d] = src_w[d];
+  const int g = lane >> 4;                  // scale group of this lane's two dimensions
+  pair[threadIdx.x] = make_double2(code_value2(threadIdx.x & 15), code_value2(threadIdx.x >> 4));
+  // codes [H][64] (16-byte loads: vals is 16-byte aligned) and, lane h, head
+  // h's weight and 4 scales, all loads issued before any is used (few rows,
+  // as in decode, are latency-bound); per (head, group) the factor
+  // (w / 2) * 2^(scale - 127), halved again because the codes are 2 |x|
+  const uint4* src_v = reinterpret_cast<const uint4*>(q.vals + (size_t)rr * H * kValBytes);
+  constexpr int kLoads = kFoldMaxHeads * (kValBytes / 16) / 64;
+  uint4 cv[kLoads];
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) cv[k] = src_v[min(lane + 64 * k, H * (kValBytes / 16) - 1)];
+  uint32_t sc4;
+  float w;
+  {
+    const int h = min(lane, H - 1);
+    sc4 = *reinterpret_cast<const uint32_t*>(q.scales + ((size_t)rr * H + h) * kScaleBytes);
+    w = q.w[(size_t)rr * H + h];
   }
+  // (slots of heads >= H get copies and are never read)
+#pragma unroll
+  for (int k = 0; k < kLoads; ++k) stage[wave][lane + 64 * k] = cv[k];
+#pragma unroll
+  for (int gg = 0; gg < kScaleBytes; ++gg)
+    hscale[wave][lane * kScaleBytes + gg] = ldexp(0.5 * (double)w, (int)((sc4 >> (8 * gg)) & 255u) - 128);
   __syncthreads();
-  const uint8_t* vrow = sb + (d >> 1);
-  const uint8_t* srow = sb + vb + g;
-  const float* wrow = reinterpret_cast<const float*>(sb + vb + scb);
-  const int nib = 4 * (d & 1);
+  const uint8_t* cb = reinterpret_cast<const uint8_t*>(stage[wave]) + lane;
+  const double* hs = hscale[wave] + g;
   // qf[d] = sum_h (w_h / 2) q_h[d], exact products, fp64 sums in head order
-  double r = 0.0;
+  double r0 = 0.0, r1 = 0.0;
 #pragma unroll 8
   for (int h = 0; h < H; ++h) {
-    const int code = (vrow[h * kValBytes] >> nib) & 15;
-    // (w/2) * 2^(scale - 127), halved again because the codes below are 2|x|
-    const double ws = ldexp(0.5 * (double)wrow[h], (int)srow[h * kScaleBytes] - 128);
-    const int m2 = (0xC8643210u >> (4 * (code & 7))) & 15;   // 2 * |e2m1 value|
-    r = fma(ws, (double)((code & 8) ? -m2 : m2), r);
+    const double f = hs[h * kScaleBytes];
+    const double2 v = pair[cb[h * kValBytes]];
+    r0 = fma(f, v.x, r0);
+    r1 = fma(f, v.y, r1);
   }
   uint8_t* orow = out + (size_t)row * kFoldRowBytes;
   for (int t = 0; t < kFoldTerms; ++t) {
-    double m = fabs(r);
+    double m = fmax(fabs(r0), fabs(r1));
     m = fmax(m, dpp_d<0xB1>(m));    // quad_perm [1,0,3,2]
     m = fmax(m, dpp_d<0x4E>(m));    // quad_perm [2,3,0,1]
     m = fmax(m, dpp_d<0x141>(m));   // row_half_mirror: 8 lanes
-    m = fmax(m, dpp_d<0x140>(m));   // row_mirror: 16 lanes
-    m = max16_d(m);                 // the group's 32 lanes
+    m = fmax(m, dpp_d<0x140>(m));   // row_mirror: the group's 16 lanes
     int e = -127;
     if (m > 0.0) {
       // ceil(log2(m / 6)) with m = f 2^x, f in [0.5, 1): x - 3 if f <= 3/4,
@@ -116,13 +114,15 @@ __global__ __launch_bounds__(256) void fold_query_kernel(QueryArgs q, uint8_t* _
       e = f <= 0.75 ? x - 3 : x - 2;
       e = e < -127 ? -127 : (e > 127 ? 127 : e);
     }
-    int code = e2m1_nearest(ldexp(fabs(r), -e));
-    if (r < 0.0 && code != 0) code |= 8;
-    r -= ldexp(e2m1_value(code), e);
-    // byte d / 2 holds dimensions d (low nibble) and d + 1 (high nibble)
-    const int partner = __builtin_amdgcn_mov_dpp(code, 0xB1, 0xf, 0xf, true);
-    if (live && (d & 1) == 0) orow[t * kValBytes + (d >> 1)] = (uint8_t)(code | (partner << 4));
-    if (live && (d & 31) == 0) orow[kFoldTerms * kValBytes + t * kScaleBytes + g] = (uint8_t)(e + 127);
+    int c0 = e2m1_nearest(ldexp(fabs(r0), -e));
+    int c1 = e2m1_nearest(ldexp(fabs(r1), -e));
+    if (r0 < 0.0 && c0 != 0) c0 |= 8;
+    if (r1 < 0.0 && c1 != 0) c1 |= 8;
+    r0 -= ldexp(code_value2(c0), e - 1);   // the code's value times 2^e, exactly
+    r1 -= ldexp(code_value2(c1), e - 1);
+    // byte l holds dimensions 2 l (low nibble) and 2 l + 1 (high nibble)
+    if (live) orow[t * kValBytes + lane] = (uint8_t)(c0 | (c1 << 4));
+    if (live && (lane & 15) == 0) orow[kFoldTerms * kValBytes + t * kScaleBytes + g] = (uint8_t)(e + 127);
   }
 }
 
