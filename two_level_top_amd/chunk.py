@@ -9,9 +9,12 @@ CandidateOverlap fork/join; prefill PR, "Level one"):
   side stream   waits "scores ready"; (idx_amax8_varlen when the keys were
                 not fused,) idx_topk_blocks, idx_expand_candidates, which
                 records table.ready
-  main stream   source's own top-k (waits table.ready when it reads the
-                table), then per consumer idx_score_sparse_paged (waits
-                table.ready inside the call) and idx_topk_rows.
+  side stream   then the source's own top-k (it reads the table the same
+                stream wrote), recording "source done"
+  main stream   per consumer idx_score_sparse_paged (waits table.ready inside
+                the call) and idx_topk_rows; finally waits "source done".
+                The source's top-k gathers S from HBM while the first
+                consumer's scores keep the MFMA and VALU busy.
 
 Every table buffer is allocated on the main stream before the fork and
 record_stream'ed to the side stream that writes it, so the caching allocator
@@ -55,7 +58,8 @@ class Chunk:
     OVERLAP_MAX_ROWS = 256
 
     def __init__(self, wl, device="cuda", n_consumers=None, k_source=None, with_offset=True,
-                 share_T=True, fused_keys=True, consumer_bf16=False, overlap_selects=None):
+                 share_T=True, fused_keys=True, consumer_bf16=False, overlap_selects=None,
+                 source_side=True):
         self.wl = wl
         self.fused_keys = fused_keys
         self.consumer_bf16 = consumer_bf16   # consumers write and select bf16 scores
@@ -84,6 +88,8 @@ class Chunk:
         self.side = torch.cuda.Stream(device=device)
         self.scores_ready = torch.cuda.Event()
         self.sel = torch.cuda.Stream(device=device) if self.overlap else None
+        self.source_side = source_side   # big tables: source top-k on the side stream
+        self.source_done = torch.cuda.Event()
         self.sparse_done = [torch.cuda.Event() for _ in range(ncons)]
         self.select_done = [torch.cuda.Event() for _ in range(ncons)]
         self.recorder = None     # optional: object with mark(name) (timing only)
@@ -109,7 +115,8 @@ class Chunk:
         self.scores_ready.record(main)
         self.side.wait_event(self.scores_ready)
         if not torch.cuda.is_current_stream_capturing():   # (a graph keeps its buffers alive)
-            for t in (self.S, self.keys, *self.table.tensors(), self.rows.req, self.rows.len):
+            for t in (self.S, self.keys, *self.table.tensors(), self.rows.req, self.rows.len,
+                      self.src_top, *((self.rows.pos_offset,) if self.rows.pos_offset is not None else ())):
                 t.record_stream(self.side)
         with torch.cuda.stream(self.side):
             if not self.fused_keys:
@@ -161,6 +168,18 @@ class Chunk:
         self.score_source()
         self.publish()
         if not self.overlap:
+            if self.source_side:
+                # the source's own top-k (HBM-bound: it gathers S at the
+                # candidates) behind the expansion on the side stream, beside
+                # the first consumer's scores (MFMA/VALU-bound)
+                main = torch.cuda.current_stream()
+                with torch.cuda.stream(self.side):
+                    self.source_topk()
+                    self.source_done.record(self.side)
+                for i in range(len(self.cons_top)):
+                    self.consumer(i)
+                main.wait_event(self.source_done)
+                return
             self.source_topk()
             for i in range(len(self.cons_top)):
                 self.consumer(i)
