@@ -208,9 +208,10 @@ idx_status idx_q_rope_quant(const uint16_t* q, const int32_t* positions, const f
  *   keys[r * ldk + i] = max(S[r*ld + 8i .. 8i+7]) for i < nblk - 1,
  *   keys[r * ldk + nblk - 1] = +inf,          nblk = ceil(len[r] / 8);
  *   rows with nblk <= skip_le_blocks are left untouched (0 = never skip).
- * ld % 8 == 0 and S 32-byte aligned (every block is one 32-byte load).
- * Device precondition: nblk <= ldk for every row.  NaN scores are ignored by
- * the max (outside the contract).
+ * ld % 8 == 0 and S 32-byte aligned (every block is one 32-byte load), else
+ * IDX_E_ALIGN; ld and ldk at most 2^29 (a row below 2 GiB), else IDX_E_ARG.
+ * Device precondition: nblk <= ldk for every row (a longer row is cut at
+ * min(ldk, ld / 8) keys).  NaN scores are outside the contract.
  */
 idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int32_t rows,
                             float* keys, int64_t ldk, int32_t skip_le_blocks, hipStream_t stream);

@@ -200,7 +200,9 @@ idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int3
   if (skip_le_blocks < 0) return fail(IDX_E_ARG, "%s: skip_le_blocks < 0", fn);
   if (ld < idxk::kBlock || ld % idxk::kBlock != 0)
     return fail(IDX_E_ALIGN, "%s: ld %lld must be a positive multiple of 8 (32-byte blocks)", fn, (long long)ld);
+  if (ld > kMaxScoreLd) return fail(IDX_E_ARG, "%s: ld %lld above 2^29", fn, (long long)ld);
   if (ldk < 1) return fail(IDX_E_ARG, "%s: ldk must hold at least one key per row", fn);
+  if (ldk > kMaxScoreLd) return fail(IDX_E_ARG, "%s: ldk %lld above 2^29", fn, (long long)ldk);
   if (rows == 0) return ok();
   if (!S || !len || !keys) return fail(IDX_E_ARG, "%s: S/len/keys is NULL", fn);
   if (!aligned(S, 32)) return fail(IDX_E_ALIGN, "%s: S must be 32-byte aligned", fn);
