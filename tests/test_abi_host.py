@@ -63,9 +63,10 @@ def test_amax8_validation(lib):
     assert lib.idx_amax8_varlen(None, 16, FAKE, 4, FAKE, 4, 0, None) == -1
     assert lib.idx_amax8_varlen(FAKE, 16, FAKE, -1, FAKE, 4, 0, None) == -1
     assert lib.idx_amax8_varlen(FAKE, 16, FAKE, 4, FAKE, 0, 0, None) == -1     # ldk < 1
-    assert lib.idx_amax8_varlen(FAKE, 16, FAKE, 0, FAKE, 4, 0, None) == 0       # nothing to do
     assert lib.idx_amax8_varlen(FAKE, 1 << 30, FAKE, 4, FAKE, 4, 0, None) == -1  # row above 2^29
+    assert "above 2^29" in _err(lib)
     assert lib.idx_amax8_varlen(FAKE, 16, FAKE, 4, FAKE, 1 << 30, 0, None) == -1  # ldk above 2^29
+    assert lib.idx_amax8_varlen(FAKE, 16, FAKE, 0, FAKE, 4, 0, None) == 0       # nothing to do
     assert _err(lib) == ""
 
 
