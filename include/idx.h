@@ -263,8 +263,9 @@ idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_
 /*
  * idx_score_sparse_paged -- a consumer's scores at its candidate positions
  * only (prefill PR, "Level two": scores written [tokens, kb*8] in ascending
- * block order, read straight from the paged pool).  Makes `stream` wait on
- * tbl->ready first (if set).
+ * block order, read straight from the paged pool).  Enqueues the query fold
+ * into ws, then makes `stream` wait on tbl->ready (if set) before the scores,
+ * so the fold may run while another stream still builds the table.
  *   T[r * ld + c] = score'(r, blocks[r][c/8]*8 + c%8) for c < valid_len[r];
  *   T beyond valid_len[r] is not written.
  * q->rows == tbl->rows; ld >= tbl->kb * 8; the pool must be under 4 GiB

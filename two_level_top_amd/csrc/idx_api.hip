@@ -256,15 +256,19 @@ static idx_status score_sparse_impl(const idx_query* q, const idx_kpool* kp, con
   if (tbl->rows > 0 && !T) return fail(IDX_E_ARG, "%s: T is NULL", fn);
   if (!aligned(T, bf16 ? 2 : 4)) return fail(IDX_E_ALIGN, "%s: T must be %d-byte aligned", fn, bf16 ? 2 : 4);
   TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
+  // the query fold reads only the query: it is enqueued before the wait on
+  // the table, so it can run while the table is still being built
+  idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
+  uint8_t* fold = static_cast<uint8_t*>(ws);
+  if (tbl->rows > 0) {
+    hipError_t e = idxk::launch_fold_query(qa, fold, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
   if (tbl->ready) {
     hipError_t e = hipStreamWaitEvent(stream, tbl->ready, 0);
     if (e != hipSuccess) return hip_status(e, "hipStreamWaitEvent on the table's ready event");
   }
   if (tbl->rows == 0) return ok();
-  idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
-  uint8_t* fold = static_cast<uint8_t*>(ws);
-  hipError_t e = idxk::launch_fold_query(qa, fold, stream);
-  if (e != hipSuccess) return hip_status(e, fn);
   return hip_status(idxk::launch_score_sparse(qa, fold, kp->pool, kp->num_pages, tbl->phys, tbl->n_kept,
                                               tbl->valid_len, tbl->rows, tbl->kb, tbl->schedule, T,
                                               ld, bf16, stream), fn);
