@@ -41,8 +41,8 @@ __device__ __forceinline__ double dpp_d(double v) {
 // are staged in LDS, together with the factor (w_h / 4) 2^(scale_hg - 127) of
 // every (head, group) and a table giving each code byte's two values as
 // 2 |e2m1| with its sign (hence the extra halving), so the head loop is two
-// LDS reads and one FMA per dimension.  The fp64 operations and their order are those of a plain
-// per-dimension loop over the heads.
+// LDS reads and one FMA per dimension.  The fp64 operations and their order
+// are those of a plain per-dimension loop over the heads.
 constexpr int kFoldRowsPerWG = 4;
 constexpr int kFoldMaxHeads = 64;
 
