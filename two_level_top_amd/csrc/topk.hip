@@ -26,6 +26,11 @@
 // instructions per element, which every pass over the registers keeps to a
 // few.
 //
+//   0. (rows held in registers) a sampled bound: the steps below run on a
+//      sample of two keys per thread to pick a bound that between k and the
+//      list's capacity elements reach, checked by one counting pass; then
+//      step 2 runs at once and step 3 finds K on the list from the top bit
+//      down.  A row whose sample does not give such a bound takes steps 1-3.
 //   1. threshold bin: one histogram pass over the digit
 //      1 + ((key - kmin) >> shift), kmin/kmax being the finite extremes of the
 //      row and shift the smallest one that fits the span in 2046 bins (-inf
@@ -409,16 +414,17 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
   // ---- 0. resident rows: a threshold from a sample ----
   // Two keys per thread, spread over each wave's slice, go through the same
   // adaptive histogram as the whole row would (section 1 below), and the
-  // lower edge of the bin holding the sample's r-th largest key, r about
-  // 1.4 k / 16 (the sample is 1/16 of a full chunk), becomes the list's
-  // bound: about 1.4 k elements of the row are expected at or above it.  One
+  // lower edge of the bin holding the sample's r-th largest key, r = k / 16
+  // plus three standard deviations (the sample is 1/16 of a full chunk),
+  // becomes the list's bound: k (1 + 3 / sqrt(k / 16)) elements of the row
+  // are expected at or above it.  One
   // counting pass checks that at least k and at most the list's capacity
   // are; then the list pass runs at once, and K is found on the list alone
   // (its bits from the top, 11 per pass).  Otherwise -- a sample too small or
   // too skewed, the k-th key at -inf -- the row takes the path below.  The
   // extremes and histogram passes over every element (and their LDS
   // atomics) are skipped; the result is the same.  (Long chunk: block
-  // top-2048 0.99 -> 0.88 ms, consumer top-512 0.39 -> 0.36 ms.  The gathered
+  // top-2048 0.99 -> 0.84 ms, consumer top-512 0.39 -> 0.36 ms.  The gathered
   // mode, bound by its scattered loads, spilled more with it and ran 25%
   // slower, so it keeps the full path.)
   if (RESIDENT && kSampledBound && MODE != MODE_GATHER) {
@@ -466,7 +472,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
     atomicAdd(&sh.hist[min(__builtin_elementwise_sub_sat(sa, slo), stop) >> sshift], 1u);
     atomicAdd(&sh.hist[min(__builtin_elementwise_sub_sat(sb, slo), stop) >> sshift], 1u);
     __syncthreads();
-    const uint32_t r = min((uint32_t)(2 * THREADS), ((uint32_t)k * 7u + 79u) / 80u);
+    // r = k/16 plus three standard deviations of the sample's count
+    const float kq = (float)k * (1.0f / 16.0f);
+    const uint32_t r = min((uint32_t)(2 * THREADS), (uint32_t)(kq + 3.0f * __builtin_sqrtf(kq)) + 1u);
     uint32_t sab, scnt;
     const uint32_t sbin = (uint32_t)find_bin<THREADS>(sh, r, &sab, &scnt);
     const uint32_t theta = sbin == 0u ? kPosInf : (sbin >= sinf ? kPosInf : slo + (sbin << sshift));
