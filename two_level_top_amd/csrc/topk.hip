@@ -417,16 +417,16 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
   // lower edge of the bin holding the sample's r-th largest key, r = k / 16
   // plus three standard deviations (the sample is 1/16 of a full chunk),
   // becomes the list's bound: k (1 + 3 / sqrt(k / 16)) elements of the row
-  // are expected at or above it.  One
-  // counting pass checks that at least k and at most the list's capacity
-  // are; then the list pass runs at once, and K is found on the list alone
-  // (its bits from the top, 11 per pass).  Otherwise -- a sample too small or
-  // too skewed, the k-th key at -inf -- the row takes the path below.  The
-  // extremes and histogram passes over every element (and their LDS
-  // atomics) are skipped; the result is the same.  (Long chunk: block
-  // top-2048 0.99 -> 0.84 ms, consumer top-512 0.39 -> 0.36 ms.  The gathered
-  // mode, bound by its scattered loads, spilled more with it and ran 25%
-  // slower, so it keeps the full path.)
+  // are expected at or above it.  One counting pass checks that at least k
+  // and at most the list's capacity are; then the list pass runs at once,
+  // and K is found on the list alone (its bits from the top, 11 per pass).
+  // Otherwise -- a sample too small or too skewed, the k-th key at -inf --
+  // the row takes the path below.  The extremes and histogram passes over
+  // every element (and their LDS atomics) are skipped; the result is the
+  // same.  (Long chunk: block top-2048 0.99 -> 0.84 ms, consumer top-512
+  // 0.39 -> 0.36 ms.  The gathered mode, bound by its scattered loads, ran
+  // 25% slower with it, whatever the sample positions, so it keeps the full
+  // path.)
   if (RESIDENT && kSampledBound && MODE != MODE_GATHER) {
     const uint32_t sa = key[0][0], sb = key[kTopkSteps / 2][2];
     uint32_t symax = max(sa + 0x00800000u, sb + 0x00800000u);
