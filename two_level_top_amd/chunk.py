@@ -12,9 +12,10 @@ CandidateOverlap fork/join; prefill PR, "Level one"):
   side stream   then the source's own top-k (it reads the table the same
                 stream wrote), recording "source done"
   main stream   per consumer idx_score_sparse_paged (waits table.ready inside
-                the call) and idx_topk_rows; finally waits "source done".
-                The source's top-k gathers S from HBM while the first
-                consumer's scores keep the MFMA and VALU busy.
+                the call; its query fold runs before that wait) and
+                idx_topk_rows; finally waits "source done".  The source's
+                top-k gathers S from HBM while the first consumer's scores
+                keep the MFMA and VALU busy (long chunk: about 0.1 ms saved).
 
 Every table buffer is allocated on the main stream before the fork and
 record_stream'ed to the side stream that writes it, so the caching allocator
@@ -28,8 +29,9 @@ stream goes on to the next consumer's sparse scores (two score buffers, the
 main stream waiting for the select that last read a buffer before
 rewriting it); the main stream waits for the select stream at the end.  On
 64 decode rows this cut the step from 0.326 to 0.298 ms; on 2048 and 16384
-rows the sparse scores fill the GPU and the overlap gains nothing, so those
-stay serial.
+rows the sparse scores fill the GPU and moving the consumers' selects gains
+nothing (16384 rows: 34.43-34.58 ms against 34.30-34.44 ms), so there they
+stay on the main stream and only the source's top-k moves, as above.
 
 The source's own top-k is taken over its candidate columns (mode GATHER)
 when kb >= k + 1: every block holding one of the k best positions then has at
