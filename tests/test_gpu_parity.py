@@ -135,7 +135,8 @@ def test_amax8_bitexact(idx, width, kb):
     rows = 64 if width <= 65536 else 32
     S = workloads.random_matrix(width, rows, width)
     # lengths whose newest block falls at, just past or just before the
-    # boundaries of the kernel's 256-block wave slices and 1024-block workgroups
+    # boundaries of the kernel's wave slices and workgroups (which divide 256
+    # blocks)
     bounds = [8 * (kb + 256 * m) + d for m in (1, 2, 4, 5) for d in (-8, -7, 0, 1, 9)]
     lens = workloads.random_lengths(width, rows, 0, width,
                                     extra=[0, 1, 7, 8, 9, width, width - 1, 8 * kb, 8 * kb + 1, 8 * kb - 1]

@@ -4,8 +4,8 @@
 //   keys[r][i] = max(S[r][8i .. 8i+7]) for i < nblk - 1, keys[r][nblk-1] = +inf,
 //   rows with nblk <= skip untouched.
 //
-// Pure HBM stream.  A wave owns 256 consecutive blocks (8 KB) and reads them
-// with 8 fully coalesced 16-byte loads per lane, all in flight at once: in
+// Pure HBM stream.  A wave owns 64 consecutive blocks (2 KB) and reads them
+// with 2 fully coalesced 16-byte loads per lane, both in flight at once: in
 // load j lane l holds half (l & 1) of block 32 j + l / 2, so every load
 // instruction covers one contiguous 1 KB.  A lane takes the max of its 4
 // values and one DPP max with its neighbour gives the block's key in the
@@ -15,18 +15,20 @@
 // blocks past the row's end read as 0 and are not stored.  Loads and stores
 // are non-temporal (neither is reused).
 //
-// Measured on MI355X (long chunk, 16.6 GB read + 2.1 GB written): 3.35 ms,
-// 5.6 TB/s = 70% of the 8 TB/s peak.  The same pass without its stores reads
-// at 6.2 TB/s; with cached loads and stores it took 3.66 ms, and 16 loads per
-// lane or one LDS-transposed 16-byte store per lane gained nothing.
+// Measured on MI355X (long chunk, 16.6 GB read + 2.1 GB written): 2.91 ms,
+// 6.4 TB/s = 80% of the 8 TB/s peak, with 2 loads per lane in workgroups of
+// 2 waves.  Per lane, 1 load ran at 72%, 4 at 74%, 8 at 70% (16 no better);
+// at 2 loads, workgroups of 1, 4 and 8 waves ran at 76%, 80% and 77%.  With
+// cached loads and stores (8 loads per lane) it took 3.66 ms; one
+// LDS-transposed 16-byte key store per lane gained nothing.
 #include "idx_internal.h"
 
 namespace idxk {
 
-constexpr int kAmaxThreads = 256;
-constexpr int kAmaxLoads = 8;                                   // 16-byte loads per lane
-constexpr int kAmaxWaveBlocks = kAmaxLoads * 32;                // 256
-constexpr int kAmaxKeys = kAmaxThreads / 64 * kAmaxWaveBlocks;  // 1024 blocks per workgroup
+constexpr int kAmaxThreads = 128;
+constexpr int kAmaxLoads = 2;                                   // 16-byte loads per lane
+constexpr int kAmaxWaveBlocks = kAmaxLoads * 32;                // 64
+constexpr int kAmaxKeys = kAmaxThreads / 64 * kAmaxWaveBlocks;  // 128 blocks per workgroup
 constexpr int kNonTemporal = 2;                                 // buffer op cache policy: nt
 
 // max of 4 floats, then of the pair of lanes (l, l ^ 1) in both lanes; written
