@@ -54,6 +54,8 @@ def workload(name):
         return workloads.prefill(), "prefill: 2048 rows x 65536 context (len 63488+i), H=64, kb=2048, 4 consumers, top-512"
     if name == "decode":
         return workloads.decode(), "decode: 64 requests x 1 row, context U[4096,65536], H=64, kb=2048, 4 consumers, top-512"
+    if name == "decode_mtp":
+        return workloads.decode_mtp(), "decode MTP: 64 requests x 2 rows (len C-1, C), C U[4096,65536], H=64, kb=2048, 4 consumers, top-512"
     if name == "tiny":
         return workloads.tiny(), "tiny: 64 rows x 1024 context, H=8, kb=16, 2 consumers, top-32"
     raise SystemExit(f"unknown config {name}")
@@ -156,8 +158,19 @@ def time_amax8(ch, bytes_per_call, reps=5):
             "note": "the unfused block-key pass over the chunk's S, timed apart from the chunk"}
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, n_rows):
     """The oracle, as it stands, on n_rows evenly spaced rows of the same chunk."""
+    import ctypes
     import numpy as np
     import oracle
     rows = np.unique(np.linspace(0, wl.rows - 1, n_rows).astype(np.int64))
@@ -165,9 +178,12 @@ def cpu_baseline(wl, n_rows):
     t0 = time.perf_counter()
     oracle.run_chunk(wl, row_ids=rows)
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    try:   # the OpenMP runtime the oracle's C code runs on reports its thread count
+        cores = int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+    except OSError:
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(len(rows) / dt, 3), "unit": "query-rows/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": _cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{len(rows)} evenly spaced rows of the same chunk, source + "
                       f"{len(wl.layers) - 1} consumers (all steps), {dt:.1f} s"}
 
@@ -177,8 +193,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "tiny"])
-    ap.add_argument("--cpu-rows", type=int, default=192,
+    ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "decode_mtp", "tiny"])
+    ap.add_argument("--cpu-rows", type=int, default=256,
                     help="rows of the CPU oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="time replays of the step captured as one HIP graph (auto: on for "

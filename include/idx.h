@@ -23,9 +23,9 @@
  * --------------------------------
  * - Every pointer is a device pointer unless its name ends in _host.
  * - The caller owns every buffer, stream and event.  The library never
- *   allocates or frees device memory and never synchronises the device
- *   (one exception: idx_prefill_tail waits for its own small host-to-device
- *   copy of the tail row list on its stream).
+ *   allocates or frees device memory and never synchronises the host with
+ *   the device: every call only enqueues kernels, event records and event
+ *   waits, so any sequence of calls can be captured into a HIP graph.
  * - Every call validates its arguments on the host before enqueuing anything;
  *   on error it returns a negative idx_status, enqueues nothing, and
  *   idx_last_error() describes the problem.  Work is asynchronous on the
@@ -156,7 +156,7 @@ enum {
   IDX_OP_TOPK_BLOCKS = 1, /* idx_topk_blocks: rows, width = ldk, k = kb     */
   IDX_OP_TOPK_ROWS = 2,   /* idx_topk_rows:   rows, width = columns, k      */
   IDX_OP_SCHEDULE = 3,    /* idx_table.schedule: rows, width = kb           */
-  IDX_OP_TAIL = 4,        /* idx_prefill_tail: rows = tail rows             */
+  IDX_OP_TAIL = 4,        /* idx_prefill_tail: rows = num_req               */
   IDX_OP_SCORE = 5        /* idx_score_dense / idx_score_sparse_paged: rows */
 };
 size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k);
@@ -333,20 +333,30 @@ idx_status idx_topk_rows_bf16(const uint16_t* X, int64_t ld, const int32_t* vali
 
 /*
  * idx_prefill_tail -- restrict a published table to the last tail_len[j] rows
- * of each request j (prefill PR, "Tail rows" and its prefill_tail; the table
- * keeps its rows' len/req so the work list can be rebuilt for the tail rows).
- * Request j owns rows [start_j, start_j + rows_per_req[j]) of `full`, starts
- * being the running sum.  tail->rows must equal sum_j tail_len[j]; tail->kb ==
- * full->kb.  Waits on full->ready, copies the rows, rebuilds tail->schedule
- * and records tail->ready.
- *   rows_per_req_host, tail_len_host: host arrays of num_req entries,
- *   0 <= tail_len[j] <= rows_per_req[j], sum rows_per_req == full->rows.
- * ws: idx_workspace_bytes(IDX_OP_TAIL, tail->rows, 0, 0) device bytes; the
- * host row list is copied into it, and the call synchronises `stream` so the
- * host copy source can be released before it returns.
+ * of each request j (prefill PR, "Tail rows" and its prefill_tail: late
+ * layers score only each request's last rows; the table keeps its rows'
+ * len/req so the work list can be rebuilt for the tail rows).
+ * Request j owns rows [start_j, start_j + rows_per_req[j]) of `full`, start_j
+ * being the running sum of rows_per_req; its tail rows are the last
+ * tail_len[j] of them, and the tail table lists every request's tail rows in
+ * row order.  Waits on full->ready (if set), copies the rows, rebuilds
+ * tail->schedule and records tail->ready.  The row list is built on the
+ * device, so the call never waits for the host and can be captured into a
+ * graph.  On the stream that built `full`, pass full->ready = NULL: a stream
+ * waiting on an event it recorded itself adds nothing, and such a wait cannot
+ * be expressed in a captured graph.
+ *   rows_per_req, tail_len: device i32 [num_req]
+ * Host checks: tail->kb == full->kb; tail->rows > 0 needs full->rows > 0 and
+ * num_req > 0.  Device preconditions (not checked, clamped): 0 <= tail_len[j]
+ * <= rows_per_req[j]; sum rows_per_req == full->rows; sum tail_len ==
+ * tail->rows.  A tail length is clamped into [0, rows_per_req[j]], a source
+ * row into the full table, and tail rows past sum tail_len are written as
+ * empty rows (n_kept = valid_len = 0).
+ * ws: idx_workspace_bytes(IDX_OP_TAIL, num_req, 0, 0) device bytes, 4-byte
+ * aligned (the per-request prefix sums); may be NULL when tail->rows == 0.
  */
-idx_status idx_prefill_tail(const idx_table* full, const int32_t* rows_per_req_host,
-                            const int32_t* tail_len_host, int32_t num_req, idx_table* tail,
+idx_status idx_prefill_tail(const idx_table* full, const int32_t* rows_per_req,
+                            const int32_t* tail_len, int32_t num_req, idx_table* tail,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

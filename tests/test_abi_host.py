@@ -149,20 +149,34 @@ def test_q_rope_quant_validation(lib):
 def test_tail_validation(lib):
     t, q, kp, rows, tbl = _structs()
     P = ctypes.byref
-    rpr = (ctypes.c_int32 * 2)(3, 1)
-    tl = (ctypes.c_int32 * 2)(2, 2)       # tail longer than its request
     tail = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 4, 16, None)
-    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail), FAKE, 64, None) == -1
-    tl = (ctypes.c_int32 * 2)(2, 1)
-    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail), FAKE, 64, None) == -3    # 3 tail rows != 4
-    tail3 = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 3, 16, None)
-    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail3), FAKE, 4, None) == -6    # workspace
-    rpr = (ctypes.c_int32 * 2)(2, 1)
-    assert lib.idx_prefill_tail(P(tbl), rpr, tl, 2, P(tail3), FAKE, 64, None) == -3   # 3 rows != 4
+    W = lib.idx_workspace_bytes(4, 2, 0, 0)
+    assert lib.idx_prefill_tail(P(tbl), FAKE, FAKE, -1, P(tail), FAKE, W, None) == -1    # num_req
+    assert lib.idx_prefill_tail(P(tbl), None, FAKE, 2, P(tail), FAKE, W, None) == -1     # no lengths
+    bad_kb = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 4, 8, None)
+    assert lib.idx_prefill_tail(P(tbl), FAKE, FAKE, 2, P(bad_kb), FAKE, W, None) == -3   # kb
+    assert lib.idx_prefill_tail(P(tbl), FAKE, FAKE, 0, P(tail), FAKE, W, None) == -3     # no requests
+    empty = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 0, 16, None)
+    assert lib.idx_prefill_tail(P(empty), FAKE, FAKE, 2, P(tail), FAKE, W, None) == -3   # no source rows
+    assert lib.idx_prefill_tail(P(tbl), FAKE, FAKE, 2, P(tail), FAKE, W - 4, None) == -6  # workspace
+    assert lib.idx_prefill_tail(P(tbl), FAKE, FAKE, 2, P(tail), FAKE_ODD2, W, None) == -2  # alignment
+    small = t._Table(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4, 16, None)
+    assert lib.idx_prefill_tail(P(tbl), FAKE, FAKE, 2, P(small), FAKE, W, None) == -6   # schedule
+
+
+def test_library_never_synchronises():
+    """Every call only enqueues work: no host-side wait on a stream, event or
+    the device anywhere in the library's sources (so calls can be captured)."""
+    csrc = os.path.join(ROOT, "two_level_top_amd", "csrc")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        for call in ("Synchronize", "hipMemcpy", "hipMalloc", "hipFree", "hipEventQuery",
+                     "hipStreamQuery"):
+            assert call not in text, f"{name} calls {call}"
 
 
 def test_workspace_sizes(lib):
     assert lib.idx_workspace_bytes(3, 16384, 2048, 0) == 16 + 16384 * 32 * 8
-    assert lib.idx_workspace_bytes(4, 100, 0, 0) == 400
+    assert lib.idx_workspace_bytes(4, 100, 0, 0) == (2 * 100 + 1) * 4 + 12   # 16-byte multiple
     assert lib.idx_workspace_bytes(1, 100, 32768, 2048) == 0
     assert lib.idx_workspace_bytes(5, 100, 0, 0) == 100 * 1088

@@ -538,6 +538,91 @@ def test_expand_and_sparse_scores(idx, name):
     assert np.isnan(Tbg[~m]).all(), "bf16 scores written past valid_len"
 
 
+def _sparse_launch(rows, kb):
+    """The consumer scorer's launch shape (score_sparse.hip): units per wave, or
+    waves per unit, from the number of 64-block work units."""
+    units = rows * ((kb + 63) // 64)
+    if units >= 2048 * 8:
+        return "upw", 8
+    if units >= 2048:
+        return "upw", units // 2048
+    split = 1
+    while split < 8 and units * split < 2048:
+        split *= 2
+    return "split", split
+
+
+# (rows, kb, context, heads): every launch shape of the consumer scorer --
+# split 8 / 4 / 2, one unit per wave, 2..8 units per wave, with a row's units
+# dividing evenly among waves (kb = 2048: 32 units) or waves spanning two rows
+# (kb = 64, 192, 320, and 7 units per wave over 32-unit rows)
+SPARSE_CASES = [
+    (8, 1024, 9000, 64),      # split 8
+    (16, 2048, 20000, 64),    # split 4
+    (40, 2048, 20000, 24),    # split 2, three 16-head blocks
+    (64, 2048, 20000, 8),     # one unit per wave, one 16-head block
+    (256, 2048, 20000, 64),   # 4 units per wave, a row's 32 units split evenly
+    (448, 2048, 20000, 64),   # 7 units per wave: waves span rows
+    (4096, 64, 2000, 64),     # 2 units per wave of 1 unit per row: two rows per wave
+    (1000, 320, 4000, 64),    # 2 units per wave over 5-unit rows
+    (5462, 192, 3000, 64),    # 8 units per wave over 3-unit rows
+]
+
+
+@pytest.mark.parametrize("rows,kb,ctx,heads", SPARSE_CASES)
+def test_sparse_scores_every_launch_shape(idx, rows, kb, ctx, heads):
+    """idx_expand_candidates and idx_score_sparse_paged against the oracle at
+    every launch shape of the scorer: expansion bit-exact on every row, scores
+    element by element on sampled rows (the first and last rows, rows where a
+    wave's units change row, random rows), nothing written past valid_len."""
+    from two_level_top_amd.chunk import Chunk
+    nreq = 4
+    per = [rows // nreq + (1 if j < rows % nreq else 0) for j in range(nreq)]
+    extra = [0, 1, 7, 8, 9, 8 * kb - 1, 8 * kb, 8 * kb + 1, ctx, ctx - 1]
+    lens = workloads.random_lengths(rows + kb, rows, 0, ctx, extra=[e for e in extra if e <= ctx])
+    starts = np.concatenate([[0], np.cumsum(per)])
+    wl = workloads.custom(f"sparse{rows}x{kb}", 70 + rows % 97, heads, kb, 32, [ctx] * nreq, per,
+                          [lens[starts[j]:starts[j + 1]] for j in range(nreq)], n_layers=2)
+    mode = _sparse_launch(rows, kb)
+    say(f"sparse scores rows={rows} kb={kb} heads={heads} launch={mode}")
+    ldk = wl.ldk
+    keys = workloads.random_matrix(rows * 3 + kb, rows, ldk)
+    keys[np.isposinf(keys)] = 1e30                 # +inf only on the newest block
+    nblk = oracle.nblocks(wl.lens)
+    for r in range(rows):
+        if nblk[r] > 0:
+            keys[r, nblk[r] - 1] = np.inf       # a keyed row's newest block
+    blocks, n_kept = oracle.select_blocks(keys, wl.lens, kb)
+    ch = Chunk(wl, n_consumers=1)
+    _table_from_oracle(idx, ch, blocks, n_kept)
+    phys_o, valid_o = oracle.expand(blocks, n_kept, wl.lens, wl.req, wl.page_table)
+    assert np.array_equal(host(ch.table.phys), phys_o)
+    assert np.array_equal(host(ch.table.valid_len), valid_o)
+    T = torch.full((rows, kb * 8), float("nan"), dtype=torch.float32, device="cuda")
+    idx.idx_score_sparse_paged(ch.queries[1], ch.kp, ch.table, T)
+    Tg = host(T)
+    U = (kb + 63) // 64
+    if mode[0] == "upw":
+        # rows whose units start or end inside a wave's run of units
+        edges = np.unique(np.arange(0, rows * U, mode[1]) // U)
+    else:
+        edges = np.arange(0, rows, max(1, rows // 16))
+    rng = np.random.default_rng(rows + kb)
+    pick = np.concatenate([np.arange(min(rows, 12)), np.arange(max(0, rows - 6), rows),
+                           edges[:48], rng.choice(rows, size=min(rows, 48), replace=False)])
+    check = np.unique(pick)
+    pos = oracle.candidate_positions(blocks, valid_o)
+    L1 = wl.layers[1]
+    To = oracle.scores_at(L1.qv, L1.qs, L1.w, wl.req, pos[check], wl.pool, wl.page_table,
+                          row_ids=check)
+    m = pos[check] >= 0
+    assert m.any()
+    assert_close(Tg[check], To, m, f"sparse rows={rows} kb={kb}")
+    assert np.isnan(Tg[check][~m]).all(), "sparse scores written past valid_len"
+    assert np.isnan(Tg[~(np.arange(kb * 8)[None, :] < valid_o[:, None])]).all(), \
+        "sparse scores written past valid_len"
+
+
 # ---------------------------------------------------------------------------
 # the whole chunk
 # ---------------------------------------------------------------------------
@@ -550,7 +635,33 @@ def _run_chunk(idx, wl, n_consumers=None):
     return ch
 
 
+def _consumer_views(ch, n_cons):
+    """Per consumer: (output row of each chunk row or None, its score buffer if
+    that buffer still holds this consumer's scores, else None)."""
+    nT = len(ch.T)
+    full_last = {}
+    tail_last = None
+    for c in range(n_cons):
+        if ch._is_tail(c):
+            tail_last = c
+        else:
+            full_last[c % nT] = c
+    out = []
+    tail_pos = {int(r): i for i, r in enumerate(ch.tail_rows)} if ch.tail is not None else {}
+    for c in range(n_cons):
+        if ch._is_tail(c):
+            out.append((tail_pos.get, ch.T_tail if tail_last == c else None))
+        else:
+            out.append((lambda r: r, ch.T[c % nT] if full_last.get(c % nT) == c else None))
+    return out
+
+
 def _check_chunk(wl, ch, rows, n_consumers):
+    """Every step of a chunk against the oracle on the sampled rows: dense scores
+    within tolerance; blocks, n_kept and valid lengths bit-exact (blocks up to
+    ties within tolerance of the kb-th key); the source's and every consumer's
+    selection up to ties within tolerance of the k-th score; and the consumer
+    scores still held in the chunk's score buffers element by element."""
     res = oracle.run_chunk(wl, row_ids=rows, n_consumers=n_consumers)
     Sg = host(ch.S)[rows]
     valid = np.arange(wl.ld)[None, :] < wl.lens[rows][:, None]
@@ -559,8 +670,11 @@ def _check_chunk(wl, ch, rows, n_consumers):
     n_kept_g = host(ch.table.n_kept)[rows]
     valid_g = host(ch.table.valid_len)[rows]
     src_g = host(ch.src_top)[rows]
-    cons_g = [host(t)[rows] for t in ch.cons_top]
+    views = _consumer_views(ch, len(ch.cons_top))
+    cons_all = [host(t) for t in ch.cons_top]
+    T_all = [None if (T is None or ch.consumer_bf16) else host(T) for _, T in views]
     same_blocks = 0
+    scores_checked = 0
     for i, r in enumerate(rows):
         L, nb = int(wl.lens[r]), int(oracle.nblocks(wl.lens[r:r + 1])[0])
         assert n_kept_g[i] == res["n_kept"][i]
@@ -582,15 +696,27 @@ def _check_chunk(wl, ch, rows, n_consumers):
             same_blocks += 1
             assert valid_g[i] == res["valid_len"][i]
             off = int(wl.req_start[r])
-            for c in range(len(cons_g)):
-                T_o = res["T"][c][i, :valid_g[i]]
-                pos = res["positions"][i, :valid_g[i]]
+            v = int(valid_g[i])
+            for c, (row_of, _) in enumerate(views):
+                j = row_of(int(r))
+                if j is None:
+                    continue
+                T_o = res["T"][c][i, :v]
+                if T_all[c] is not None and v:
+                    assert_close(T_all[c][j, :v][None], T_o[None], np.ones((1, v), bool),
+                                 f"{wl.name} row {r} consumer {c} scores")
+                    scores_checked += 1
+                pos = res["positions"][i, :v]
                 score = dict(zip((pos + off).tolist(), T_o.tolist()))
-                if valid_g[i]:
+                if v:
                     kth = kth_largest(T_o, wl.kc)
-                    assert_same_selection(cons_g[c][i], res["consumer_topk"][c][i], score.get, kth, -1,
-                                          f"{wl.name} row {r} consumer {c}")
+                    assert_same_selection(cons_all[c][j], res["consumer_topk"][c][i], score.get, kth,
+                                          -1, f"{wl.name} row {r} consumer {c}")
+                else:
+                    assert (cons_all[c][j] == -1).all()
     assert same_blocks >= 0.9 * len(rows), f"only {same_blocks}/{len(rows)} rows kept identical blocks"
+    if not ch.consumer_bf16 and len(ch.cons_top):
+        assert scores_checked > 0, "no consumer scores were compared"
 
 
 def _check_bf16_agreement(wl, ch, rows, n_consumers):
@@ -713,41 +839,58 @@ def test_chunk_graph_replay(idx):
 
 
 def test_chunk_mixed_small(idx):
-    wl = workloads.mixed(n_consumers=1, decode_rows=32, max_decode_ctx=65536)
-    say(f"chunk mixed (rows {wl.rows})")
-    ch = _run_chunk(idx, wl)
+    wl = workloads.mixed(n_consumers=2, decode_rows=32, max_decode_ctx=65536)
+    say(f"chunk mixed (rows {wl.rows}), consumer 1 on the tail rows")
+    from two_level_top_amd.chunk import Chunk
+    ch = Chunk(wl, tail_layers=1)
+    ch.run()
+    torch.cuda.synchronize()
     starts = np.concatenate([[0], np.cumsum(wl.rows_per_req)])
-    rows = np.unique(np.concatenate([starts[:-1], starts[1:] - 1, np.arange(0, wl.rows, 397)]))
+    rows = np.unique(np.concatenate([starts[:-1], starts[1:] - 1, np.arange(0, wl.rows, 397),
+                                     ch.tail_rows[::29]]))
     rows = rows[rows < wl.rows]
     _check_chunk(wl, ch, rows, None)
 
 
+def _tail_case():
+    return workloads.custom("tail", 7, 16, 4, 6, [300, 200, 90, 64], [40, 3, 1, 5],
+                            [[260 + i for i in range(40)], [197, 198, 199], [90], [60, 61, 62, 63, 64]],
+                            n_layers=3, tail=[5, 3, 1, 0])
+
+
 def test_prefill_tail(idx):
+    """The tail table against the full table's rows and the oracle; the tail
+    consumer's scores and selection against the oracle's on those rows."""
     import two_level_top_amd as t
-    wl = workloads.custom("tail", 7, 16, 4, 6, [300, 200, 90, 64], [40, 3, 1, 5],
-                          [[260 + i for i in range(40)], [197, 198, 199], [90], [60, 61, 62, 63, 64]],
-                          n_layers=2, tail=[5, 3, 1, 0])
-    say("prefill tail")
-    ch = _run_chunk(idx, wl)
+    from two_level_top_amd.chunk import Chunk
+    wl = _tail_case()
+    say("prefill tail (device row list), a tail consumer layer")
+    ch = Chunk(wl, tail_layers=1)
+    ch.run()
+    torch.cuda.synchronize()
+    _check_chunk(wl, ch, np.arange(wl.rows), None)
     trows = oracle.tail_rows(wl.rows_per_req, wl.tail_len)
-    tail = t.Table(len(trows), wl.kb)
-    t.idx_prefill_tail(ch.table, wl.rows_per_req, wl.tail_len, tail)
+    assert np.array_equal(ch.tail_rows, trows)
     for name in ("blocks", "n_kept", "phys", "valid_len", "len", "req"):
-        assert np.array_equal(host(getattr(tail, name)), host(getattr(ch.table, name))[trows]), name
-    # consumer selection on the tail table = the full table's selection of those rows
-    T = torch.full((len(trows), wl.kb * 8), float("nan"), dtype=torch.float32, device="cuda")
-    L = wl.layers[1]
-    q = t.Query(dev(L.qv[trows]), dev(L.qs[trows]), dev(L.w[trows]))
-    t.idx_score_sparse_paged(q, ch.kp, tail, T)
-    out = torch.empty((len(trows), wl.kc), dtype=torch.int32, device="cuda")
-    t.idx_topk_rows(T, tail.valid_len, wl.kc, out, mode=t.COLS_BLOCKMAP, blocks=tail.blocks,
-                    pos_offset=dev(wl.req_start[trows]))
-    assert np.array_equal(host(out), host(ch.cons_top[0])[trows])
-    sched = host(tail.schedule).view(np.int32)
+        assert np.array_equal(host(getattr(ch.tail, name)), host(getattr(ch.table, name))[trows]), name
+    # (_check_chunk above compared the tail consumer's scores and selection with
+    # the oracle's on every tail row)
+    sched = host(ch.tail.schedule).view(np.int32)
     assert sched[0] == len(trows) * ((wl.kb + 63) // 64)
-    nk = host(tail.n_kept)
+    nk = host(ch.tail.n_kept)
     firsts = sched[4:4 + 2 * sched[0]].reshape(-1, 2)[:, 1]
     assert ((firsts >= 0).reshape(len(trows), -1).sum(1) == (nk + 63) // 64).all()
+    # the call on its own, from host lists, into a fresh table: same rows;
+    # tail rows beyond the tail lengths' sum come out empty
+    tail = t.Table(len(trows) + 2, wl.kb)
+    t.idx_prefill_tail(ch.table, wl.rows_per_req, wl.tail_len, tail)
+    assert np.array_equal(host(tail.blocks)[:len(trows)], host(ch.tail.blocks))
+    assert (host(tail.n_kept)[len(trows):] == 0).all() and (host(tail.valid_len)[len(trows):] == 0).all()
+    assert (host(tail.phys)[len(trows):] == -1).all()
+    # lengths past a request's rows are clamped to its rows
+    clamped = t.Table(int(wl.rows_per_req.sum()), wl.kb)
+    t.idx_prefill_tail(ch.table, wl.rows_per_req, wl.rows_per_req + 3, clamped)
+    assert np.array_equal(host(clamped.blocks), host(ch.table.blocks))
 
 
 def test_chunk_prefill_sampled(idx):
@@ -760,7 +903,8 @@ def test_chunk_prefill_sampled(idx):
 def test_chunk_long_sampled(idx):
     """The benchmarked chunk itself: 16384 rows at 262144-position context,
     source + 4 consumers, launched exactly as bench.py launches it; sampled
-    rows checked against the oracle."""
+    rows checked against the oracle, the last consumer's scores element by
+    element."""
     wl = workloads.long_chunk()
     say("chunk long 16384 x 262144, source + 4 consumers (sampled rows)")
     ch = _run_chunk(idx, wl)
@@ -769,16 +913,93 @@ def test_chunk_long_sampled(idx):
 
 def test_chunk_mixed_full(idx):
     """The mixed batch at full size: 8 prefill requests and 256 decode rows
-    up to 262144 context, duplicated K records, plus its tail table."""
-    import two_level_top_amd as t
+    up to 262144 context, duplicated K records; the last two consumers score
+    only the tail rows (min(64, n) per request) through idx_prefill_tail."""
+    from two_level_top_amd.chunk import Chunk
     wl = workloads.mixed()
-    say(f"chunk mixed full (rows {wl.rows}, pages {wl.num_pages})")
-    ch = _run_chunk(idx, wl)
+    say(f"chunk mixed full (rows {wl.rows}, pages {wl.num_pages}), 2 tail consumers")
+    ch = Chunk(wl, tail_layers=2)
+    ch.run()
+    torch.cuda.synchronize()
     starts = np.concatenate([[0], np.cumsum(wl.rows_per_req)])
-    rows = np.unique(np.concatenate([starts[:8], starts[1:9] - 1, starts[8] + np.arange(0, 256, 37)]))
+    rows = np.unique(np.concatenate([starts[:8], starts[1:9] - 1, starts[8] + np.arange(0, 256, 37),
+                                     ch.tail_rows[::61]]))
     _check_chunk(wl, ch, rows, None)
     trows = oracle.tail_rows(wl.rows_per_req, wl.tail_len)
-    tail = t.Table(len(trows), wl.kb)
-    t.idx_prefill_tail(ch.table, wl.rows_per_req, wl.tail_len, tail)
     for name in ("blocks", "n_kept", "phys", "valid_len", "len", "req"):
-        assert np.array_equal(host(getattr(tail, name)), host(getattr(ch.table, name))[trows]), name
+        assert np.array_equal(host(getattr(ch.tail, name)), host(getattr(ch.table, name))[trows]), name
+
+
+def test_chunk_graph_with_tail(idx):
+    """Publish, the tail table and the consumers (two on the full table, one on
+    the tail rows) captured as one HIP graph: every replay equals the eager
+    step bit for bit, with every output overwritten eagerly in between."""
+    from two_level_top_amd.chunk import Chunk
+    wl = workloads.mixed(n_consumers=3, decode_rows=16, max_decode_ctx=32768)
+    say(f"chunk mixed (rows {wl.rows}) with a tail consumer, captured as a HIP graph")
+    ch = Chunk(wl, tail_layers=1)
+    ch.run()
+    torch.cuda.synchronize()
+    names = ("blocks", "n_kept", "phys", "valid_len")
+    outs = lambda: [ch.src_top, *ch.cons_top, *(getattr(ch.table, n) for n in names),
+                    *(getattr(ch.tail, n) for n in names)]
+    ref = [host(x) for x in outs()]
+    ch.capture()
+    for _ in range(3):
+        for x in outs():
+            x.fill_(-7)
+        torch.cuda.synchronize()
+        ch.replay()
+        torch.cuda.synchronize()
+        for x, r in zip(outs(), ref):
+            assert np.array_equal(host(x), r)
+
+
+def test_publish_error_joins_side_stream(idx):
+    """A host-side validation error inside publish (after the block top-k was
+    already enqueued on the side stream) under graph capture: the main stream
+    rejoins the side stream before the error propagates, so the capture ends
+    cleanly and the library's own error is what the caller sees."""
+    import two_level_top_amd as t
+    from two_level_top_amd.chunk import Chunk
+    wl = workloads.tiny()
+    say("publish raising inside a graph capture")
+    ch = Chunk(wl)
+    ch.run()
+    torch.cuda.synchronize()
+    good = ch.table.schedule
+    ch.table.schedule = torch.empty((8,), dtype=torch.uint8, device="cuda")   # too small
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(t.IdxError, match="schedule_bytes"):
+        with torch.cuda.graph(g):
+            ch.score_source()
+            ch.publish()
+    ch.table.schedule = good
+    torch.cuda.synchronize()
+    ch.run()
+    torch.cuda.synchronize()
+    _check_chunk(wl, ch, np.arange(0, wl.rows, 7), None)
+
+
+def test_chunk_decode_mtp(idx):
+    """Decode with two rows per request (multi-token prediction / verify:
+    lengths C - 1 and C) against the oracle on every row; and the paired rows
+    equal the same rows scored apart from each other, bit for bit."""
+    from two_level_top_amd.chunk import Chunk
+    wl = workloads.decode_mtp(n_consumers=2)
+    say(f"chunk decode MTP ({wl.rows} rows, 2 per request)")
+    ch = Chunk(wl)
+    ch.run()
+    torch.cuda.synchronize()
+    _check_chunk(wl, ch, np.arange(wl.rows), None)
+    for parity in (0, 1):
+        sel = np.arange(parity, wl.rows, 2)
+        sub = Chunk(workloads.select_rows(wl, sel))
+        sub.run()
+        torch.cuda.synchronize()
+        idx_t = torch.from_numpy(sel).cuda()
+        assert np.array_equal(host(sub.src_top), host(ch.src_top[idx_t]))
+        for name in ("blocks", "n_kept", "valid_len"):
+            assert np.array_equal(host(getattr(sub.table, name)), host(getattr(ch.table, name)[idx_t]))
+        for a, b in zip(sub.cons_top, ch.cons_top):
+            assert np.array_equal(host(a), host(b[idx_t]))

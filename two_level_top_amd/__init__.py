@@ -24,10 +24,13 @@ __all__ = [
     "idx_score_sparse_paged", "idx_score_sparse_paged_bf16", "idx_topk_rows", "idx_topk_rows_bf16",
     "idx_prefill_tail", "idx_workspace_bytes",
     "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table", "score_workspace",
+    "tail_workspace",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libidx.so")
+# IDX_LIBRARY selects another build of the same library (e.g. a sanitizer build
+# of its host code); the default is the in-tree gfx950 build
+LIB_PATH = os.environ.get("IDX_LIBRARY") or os.path.join(HERE, "libidx.so")
 
 COLS_IDENTITY, COLS_BLOCKMAP, COLS_GATHER = 0, 1, 2
 OP_TOPK_BLOCKS, OP_TOPK_ROWS, OP_SCHEDULE, OP_TAIL, OP_SCORE = 1, 2, 3, 4, 5
@@ -143,16 +146,32 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _req(t: torch.Tensor, dtype, name: str):
+def _req(t: torch.Tensor, dtype, name: str, rows: int | None = None, gpu: bool = True):
+    """Type, dtype, contiguity and (when given) leading dimension of one operand;
+    with gpu=False the device is left to a later _on_gpu call, so that every
+    shape check of a call runs before any device check."""
     if not isinstance(t, torch.Tensor):
         raise IdxError(f"{name}: expected a tensor")
     if t.dtype != dtype:
         raise IdxError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if not t.is_contiguous():
         raise IdxError(f"{name}: must be contiguous")
-    if not t.is_cuda:
-        raise IdxError(f"{name}: must be on the GPU")
+    if rows is not None and (t.dim() == 0 or int(t.shape[0]) != rows):
+        raise IdxError(f"{name}: leading dimension {tuple(t.shape)[:1]} != {rows} rows")
+    if gpu:
+        _on_gpu(t, names=(name,))
     return t
+
+
+def _on_gpu(*ts, names=None):
+    for i, t in enumerate(ts):
+        if t is not None and not t.is_cuda:
+            raise IdxError(f"{names[i] if names else 'operand'}: must be on the GPU")
+
+
+def _width(t: torch.Tensor, need: int, name: str):
+    if t.dim() != 2 or int(t.shape[1]) < need:
+        raise IdxError(f"{name}: shape {tuple(t.shape)} needs at least {need} columns")
 
 
 # ---------------------------------------------------------------------------
@@ -163,13 +182,16 @@ class Query:
     """One index layer's query batch: vals u8 [R,H,64], scales u8 [R,H,4], w f32 [R,H]."""
 
     def __init__(self, vals, scales, w):
-        self.vals = _req(vals, torch.uint8, "vals")
-        self.scales = _req(scales, torch.uint8, "scales")
-        self.w = _req(w, torch.float32, "w")
+        self.vals = _req(vals, torch.uint8, "vals", gpu=False)
+        self.scales = _req(scales, torch.uint8, "scales", gpu=False)
+        self.w = _req(w, torch.float32, "w", gpu=False)
+        if vals.dim() != 3:
+            raise IdxError("query shapes must be [R,H,64], [R,H,4], [R,H]")
         self.rows, self.heads = int(vals.shape[0]), int(vals.shape[1])
         if tuple(vals.shape) != (self.rows, self.heads, 64) or \
            tuple(scales.shape) != (self.rows, self.heads, 4) or tuple(w.shape) != (self.rows, self.heads):
             raise IdxError("query shapes must be [R,H,64], [R,H,4], [R,H]")
+        _on_gpu(self.vals, self.scales, self.w, names=("vals", "scales", "w"))
 
     def c(self):
         return _Query(_ptr(self.vals), _ptr(self.scales), _ptr(self.w), self.rows, self.heads, 128)
@@ -179,11 +201,14 @@ class KPool:
     """Paged MXFP4 index-K pool u8 [pages, 64*68] and page table i32 [num_req, max_pages]."""
 
     def __init__(self, pool, page_table, page_size: int = 64):
-        self.pool = _req(pool, torch.uint8, "pool")
-        self.page_table = _req(page_table, torch.int32, "page_table")
+        self.pool = _req(pool, torch.uint8, "pool", gpu=False)
+        self.page_table = _req(page_table, torch.int32, "page_table", gpu=False)
         self.page_size = page_size
         if pool.dim() != 2 or pool.shape[1] != page_size * 68:
             raise IdxError("pool must be [num_pages, page_size * 68]")
+        if page_table.dim() != 2:
+            raise IdxError("page_table must be [num_req, max_pages]")
+        _on_gpu(self.pool, self.page_table, names=("pool", "page_table"))
 
     def c(self):
         return _KPool(_ptr(self.pool), int(self.pool.shape[0]), self.page_size, 128,
@@ -195,10 +220,14 @@ class Rows:
     """Per-row request ids, compress_lens and optional output offsets (all i32 [R])."""
 
     def __init__(self, req, lens, pos_offset=None):
-        self.req = _req(req, torch.int32, "req")
-        self.len = _req(lens, torch.int32, "len")
-        self.pos_offset = None if pos_offset is None else _req(pos_offset, torch.int32, "pos_offset")
+        if not isinstance(req, torch.Tensor) or req.dim() != 1:
+            raise IdxError("req must be a 1-d tensor")
         self.rows = int(req.shape[0])
+        self.req = _req(req, torch.int32, "req", gpu=False)
+        self.len = _req(lens, torch.int32, "len", rows=self.rows, gpu=False)
+        self.pos_offset = None if pos_offset is None else \
+            _req(pos_offset, torch.int32, "pos_offset", rows=self.rows, gpu=False)
+        _on_gpu(self.req, self.len, self.pos_offset, names=("req", "len", "pos_offset"))
 
     def c(self):
         return _Rows(_ptr(self.req), _ptr(self.len), _ptr(self.pos_offset), self.rows)
@@ -271,7 +300,9 @@ def _score_ws(ws, rows, device, stream):
 
 
 def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, ws=None, stream=None):
-    _req(S, torch.float32, "S")
+    if q.rows != rows.rows:
+        raise IdxError(f"query rows {q.rows} != rows {rows.rows}")
+    _req(S, torch.float32, "S", rows=rows.rows)
     ws = _score_ws(ws, q.rows, S.device, stream)
     q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
     _check(load().idx_score_dense(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
@@ -281,7 +312,11 @@ def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, ws=None, s
 
 def idx_score_dense_keys(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, keys: torch.Tensor,
                          skip_le_blocks: int = 0, ws=None, stream=None):
-    _req(S, torch.float32, "S"); _req(keys, torch.float32, "keys")
+    if q.rows != rows.rows:
+        raise IdxError(f"query rows {q.rows} != rows {rows.rows}")
+    _req(S, torch.float32, "S", rows=rows.rows, gpu=False)
+    _req(keys, torch.float32, "keys", rows=rows.rows, gpu=False)
+    _on_gpu(S, keys, names=("S", "keys"))
     ws = _score_ws(ws, q.rows, S.device, stream)
     q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
     _check(load().idx_score_dense_keys(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
@@ -294,9 +329,14 @@ def idx_q_rope_quant(q_bits: torch.Tensor, positions: torch.Tensor, cos_sin: tor
                      w: torch.Tensor, is_neox: bool, softmax_scale: float, head_scale: float,
                      vals: torch.Tensor, scales: torch.Tensor, w_out: torch.Tensor, stream=None):
     """q_bits: bf16 bit patterns as int16 [rows, heads, 128]; outputs an idx_query's arrays."""
-    _req(q_bits, torch.int16, "q"); _req(positions, torch.int32, "positions")
-    _req(cos_sin, torch.float32, "cos_sin"); _req(w, torch.float32, "w")
-    _req(vals, torch.uint8, "vals"); _req(scales, torch.uint8, "scales"); _req(w_out, torch.float32, "w_out")
+    args = {"q": (q_bits, torch.int16), "positions": (positions, torch.int32),
+            "cos_sin": (cos_sin, torch.float32), "w": (w, torch.float32),
+            "vals": (vals, torch.uint8), "scales": (scales, torch.uint8),
+            "w_out": (w_out, torch.float32)}
+    for name, (t, dt) in args.items():
+        _req(t, dt, name, gpu=False)
+    if q_bits.dim() != 3:
+        raise IdxError("q must be [rows, heads, 128]")
     rows, heads = int(q_bits.shape[0]), int(q_bits.shape[1])
     shapes = {"q": (q_bits, (rows, heads, 128)), "positions": (positions, (rows,)),
               "w": (w, (rows, heads)), "vals": (vals, (rows, heads, 64)),
@@ -306,6 +346,7 @@ def idx_q_rope_quant(q_bits: torch.Tensor, positions: torch.Tensor, cos_sin: tor
             raise IdxError(f"{name}: shape {tuple(t.shape)}, expected {shape}")
     if cos_sin.dim() != 2 or cos_sin.shape[1] != 64:
         raise IdxError("cos_sin must be [max_pos, 64]")
+    _on_gpu(*(t for t, _ in args.values()), names=tuple(args))
     _check(load().idx_q_rope_quant(_ptr(q_bits), _ptr(positions), _ptr(cos_sin), int(cos_sin.shape[0]),
                                    _ptr(w), rows, heads, 1 if is_neox else 0, float(softmax_scale),
                                    float(head_scale), _ptr(vals), _ptr(scales), _ptr(w_out),
@@ -313,30 +354,48 @@ def idx_q_rope_quant(q_bits: torch.Tensor, positions: torch.Tensor, cos_sin: tor
 
 
 def idx_amax8_varlen(S, lens, keys, skip_le_blocks: int = 0, stream=None):
-    _req(S, torch.float32, "S"); _req(lens, torch.int32, "len"); _req(keys, torch.float32, "keys")
-    _check(load().idx_amax8_varlen(_ptr(S), S.stride(0), _ptr(lens), int(lens.shape[0]), _ptr(keys),
+    _req(lens, torch.int32, "len", gpu=False)
+    n = int(lens.shape[0]) if lens.dim() == 1 else -1
+    _req(S, torch.float32, "S", rows=n, gpu=False)
+    _req(keys, torch.float32, "keys", rows=n, gpu=False)
+    _on_gpu(S, lens, keys, names=("S", "len", "keys"))
+    _check(load().idx_amax8_varlen(_ptr(S), S.stride(0), _ptr(lens), n, _ptr(keys),
                                    keys.stride(0), int(skip_le_blocks), _stream(stream)),
            "idx_amax8_varlen")
 
 
 def idx_topk_blocks(keys, lens, kb: int, blocks, n_kept, stream=None):
-    _req(keys, torch.float32, "keys"); _req(lens, torch.int32, "len")
-    _req(blocks, torch.int32, "blocks"); _req(n_kept, torch.int32, "n_kept")
-    if blocks.shape[-1] != kb:
+    _req(lens, torch.int32, "len", gpu=False)
+    n = int(lens.shape[0]) if lens.dim() == 1 else -1
+    _req(keys, torch.float32, "keys", rows=n, gpu=False)
+    _req(blocks, torch.int32, "blocks", rows=n, gpu=False)
+    _req(n_kept, torch.int32, "n_kept", rows=n, gpu=False)
+    if blocks.dim() != 2 or blocks.shape[-1] != kb:
         raise IdxError("blocks must be [rows, kb]")
-    _check(load().idx_topk_blocks(_ptr(keys), keys.stride(0), _ptr(lens), int(lens.shape[0]), kb,
+    _on_gpu(keys, lens, blocks, n_kept, names=("keys", "len", "blocks", "n_kept"))
+    _check(load().idx_topk_blocks(_ptr(keys), keys.stride(0), _ptr(lens), n, kb,
                                   _ptr(blocks), _ptr(n_kept), None, 0, _stream(stream)),
            "idx_topk_blocks")
 
 
 def idx_expand_candidates(kp: KPool, rows: Rows, tbl: Table, stream=None):
+    if tbl.rows != rows.rows:
+        raise IdxError(f"table rows {tbl.rows} != rows {rows.rows}")
     kp_c, rows_c, t_c = kp.c(), rows.c(), tbl.c()
     _check(load().idx_expand_candidates(ctypes.byref(kp_c), ctypes.byref(rows_c), ctypes.byref(t_c),
                                         _stream(stream)), "idx_expand_candidates")
 
 
+def _sparse_args(q: Query, tbl: Table, T: torch.Tensor, dtype):
+    if q.rows != tbl.rows:
+        raise IdxError(f"query rows {q.rows} != table rows {tbl.rows}")
+    _req(T, dtype, "T", rows=tbl.rows, gpu=False)
+    _width(T, tbl.kb * 8, "T")
+    _on_gpu(T, names=("T",))
+
+
 def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=None, stream=None):
-    _req(T, torch.float32, "T")
+    _sparse_args(q, tbl, T, torch.float32)
     ws = _score_ws(ws, q.rows, T.device, stream)
     q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
     _check(load().idx_score_sparse_paged(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
@@ -348,7 +407,7 @@ def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=
 def idx_score_sparse_paged_bf16(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=None,
                                 stream=None):
     """T: torch.bfloat16 [rows, >= kb * 8]."""
-    _req(T, torch.bfloat16, "T")
+    _sparse_args(q, tbl, T, torch.bfloat16)
     ws = _score_ws(ws, q.rows, T.device, stream)
     q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
     _check(load().idx_score_sparse_paged_bf16(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
@@ -357,50 +416,74 @@ def idx_score_sparse_paged_bf16(q: Query, kp: KPool, tbl: Table, T: torch.Tensor
            "idx_score_sparse_paged_bf16")
 
 
-def idx_topk_rows_bf16(X, valid, k: int, out, mode: int = COLS_IDENTITY, blocks=None,
-                       pos_offset=None, stream=None):
-    """X: torch.bfloat16 rows; as idx_topk_rows otherwise."""
-    _req(X, torch.bfloat16, "X"); _req(valid, torch.int32, "valid"); _req(out, torch.int32, "out")
-    if out.shape[-1] != k:
+def _topk_args(X, xdtype, valid, k, out, mode, blocks, pos_offset):
+    _req(valid, torch.int32, "valid", gpu=False)
+    n = int(valid.shape[0]) if valid.dim() == 1 else -1
+    _req(X, xdtype, "X", rows=n, gpu=False)
+    _req(out, torch.int32, "out", rows=n, gpu=False)
+    if out.dim() != 2 or out.shape[-1] != k:
         raise IdxError("out must be [rows, k]")
     kb = 0
     if blocks is not None:
-        _req(blocks, torch.int32, "blocks")
+        _req(blocks, torch.int32, "blocks", rows=n, gpu=False)
         kb = int(blocks.shape[-1])
+        if mode == COLS_BLOCKMAP:
+            _width(X, kb * 8, "X")
+    elif mode != COLS_IDENTITY:
+        raise IdxError("blocks are required in the block-mapped modes")
     if pos_offset is not None:
-        _req(pos_offset, torch.int32, "pos_offset")
-    _check(load().idx_topk_rows_bf16(_ptr(X), X.stride(0), _ptr(valid), int(valid.shape[0]), k, mode,
+        _req(pos_offset, torch.int32, "pos_offset", rows=n, gpu=False)
+    _on_gpu(X, valid, out, blocks, pos_offset, names=("X", "valid", "out", "blocks", "pos_offset"))
+    return n, kb
+
+
+def idx_topk_rows_bf16(X, valid, k: int, out, mode: int = COLS_IDENTITY, blocks=None,
+                       pos_offset=None, stream=None):
+    """X: torch.bfloat16 rows; as idx_topk_rows otherwise."""
+    n, kb = _topk_args(X, torch.bfloat16, valid, k, out, mode, blocks, pos_offset)
+    _check(load().idx_topk_rows_bf16(_ptr(X), X.stride(0), _ptr(valid), n, k, mode,
                                      _ptr(blocks), kb, _ptr(pos_offset), _ptr(out), None, 0,
                                      _stream(stream)), "idx_topk_rows_bf16")
 
 
 def idx_topk_rows(X, valid, k: int, out, mode: int = COLS_IDENTITY, blocks=None, pos_offset=None,
                   stream=None):
-    _req(X, torch.float32, "X"); _req(valid, torch.int32, "valid"); _req(out, torch.int32, "out")
-    if out.shape[-1] != k:
-        raise IdxError("out must be [rows, k]")
-    kb = 0
-    if blocks is not None:
-        _req(blocks, torch.int32, "blocks")
-        kb = int(blocks.shape[-1])
-    if pos_offset is not None:
-        _req(pos_offset, torch.int32, "pos_offset")
-    _check(load().idx_topk_rows(_ptr(X), X.stride(0), _ptr(valid), int(valid.shape[0]), k, mode,
+    n, kb = _topk_args(X, torch.float32, valid, k, out, mode, blocks, pos_offset)
+    _check(load().idx_topk_rows(_ptr(X), X.stride(0), _ptr(valid), n, k, mode,
                                 _ptr(blocks), kb, _ptr(pos_offset), _ptr(out), None, 0,
                                 _stream(stream)), "idx_topk_rows")
 
 
-def idx_prefill_tail(full: Table, rows_per_req, tail_len, tail: Table, ws=None, stream=None):
-    import numpy as np
-    rpr = np.ascontiguousarray(np.asarray(rows_per_req, dtype=np.int32))
-    tl = np.ascontiguousarray(np.asarray(tail_len, dtype=np.int32))
+def tail_workspace(num_req: int, device="cuda") -> torch.Tensor:
+    """Workspace of idx_prefill_tail for num_req requests."""
+    n = max(16, idx_workspace_bytes(OP_TAIL, num_req, 0, 0))
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def idx_prefill_tail(full: Table, rows_per_req, tail_len, tail: Table, ws=None, stream=None,
+                     wait_full: bool = True):
+    """rows_per_req, tail_len: int32 device tensors [num_req] (array-likes are copied to the
+    tail table's device first, which a graph capture cannot record: pass tensors there).
+    wait_full=False: the call runs on the stream that built `full`, so it does not wait
+    on full's ready event (a stream never waits on an event it recorded itself)."""
+    dev = tail.blocks.device
+    if not isinstance(rows_per_req, torch.Tensor):
+        rows_per_req = torch.as_tensor(rows_per_req, dtype=torch.int32).to(dev)
+    if not isinstance(tail_len, torch.Tensor):
+        tail_len = torch.as_tensor(tail_len, dtype=torch.int32).to(dev)
+    _req(rows_per_req, torch.int32, "rows_per_req", gpu=False)
+    num_req = int(rows_per_req.shape[0]) if rows_per_req.dim() == 1 else -1
+    _req(tail_len, torch.int32, "tail_len", rows=num_req, gpu=False)
+    _on_gpu(rows_per_req, tail_len, names=("rows_per_req", "tail_len"))
     if ws is None:
-        n = max(1, idx_workspace_bytes(OP_TAIL, tail.rows, 0, 0))
-        ws = torch.empty((n,), dtype=torch.uint8, device=tail.blocks.device)
+        ws = tail_workspace(num_req, dev)
         if stream is not None:
             ws.record_stream(stream)
+    _req(ws, torch.uint8, "ws")
     f_c, t_c = full.c(), tail.c()
-    _check(load().idx_prefill_tail(ctypes.byref(f_c), rpr.ctypes.data_as(_P), tl.ctypes.data_as(_P),
-                                   len(rpr), ctypes.byref(t_c), _ptr(ws), ws.numel(),
-                                   _stream(stream)), "idx_prefill_tail")
+    if not wait_full:
+        f_c.ready = None
+    _check(load().idx_prefill_tail(ctypes.byref(f_c), _ptr(rows_per_req), _ptr(tail_len), num_req,
+                                   ctypes.byref(t_c), _ptr(ws), ws.numel(), _stream(stream)),
+           "idx_prefill_tail")
     return ws

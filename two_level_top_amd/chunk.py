@@ -33,6 +33,16 @@ rows the sparse scores fill the GPU and moving the consumers' selects gains
 nothing (16384 rows: 34.43-34.58 ms against 34.30-34.44 ms), so there they
 stay on the main stream and only the source's top-k moves, as above.
 
+Tail layers (prefill PR, "Tail rows"): the last `tail_layers` consumers
+score only the last tail_len[j] rows of each request j.  The side stream
+builds their table with idx_prefill_tail right after the expansion (it records
+the tail table's own ready event), and those consumers wait on it.
+
+If any call raises inside a block that was forked onto the side or select
+stream, the main stream waits for that stream before the exception leaves
+(vLLM decode page, CandidateOverlap fork/join), so that a graph capture ends
+with every stream joined and reports the real error.
+
 The source's own top-k is taken over its candidate columns (mode GATHER)
 when kb >= k + 1: every block holding one of the k best positions then has at
 most k - 1 blocks above it, so the result equals the dense top-k; otherwise
@@ -41,16 +51,41 @@ the dense row is selected directly (mode IDENTITY).
 
 from __future__ import annotations
 
+import contextlib
+
+import numpy as np
 import torch
 
 from . import (COLS_BLOCKMAP, COLS_GATHER, COLS_IDENTITY, KPool, Query, Rows, Table,
-               idx_amax8_varlen, idx_expand_candidates, idx_score_dense, idx_score_dense_keys,
-               idx_score_sparse_paged, idx_score_sparse_paged_bf16, idx_topk_blocks, idx_topk_rows,
-               idx_topk_rows_bf16, score_workspace, stream_wait_table)
+               idx_amax8_varlen, idx_expand_candidates, idx_prefill_tail, idx_score_dense,
+               idx_score_dense_keys, idx_score_sparse_paged, idx_score_sparse_paged_bf16,
+               idx_topk_blocks, idx_topk_rows, idx_topk_rows_bf16, score_workspace,
+               stream_wait_table, tail_workspace)
 
 
 def _dev(a, dtype, device):
-    return torch.from_numpy(a).to(device=device, dtype=dtype).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device=device, dtype=dtype).contiguous()
+
+
+@contextlib.contextmanager
+def _forked(stream, main):
+    """Run a block on `stream`; if it raises, make `main` wait for `stream`
+    before the exception propagates (the fork is always joined)."""
+    try:
+        with torch.cuda.stream(stream):
+            yield
+    except BaseException:
+        main.wait_stream(stream)
+        raise
+
+
+def tail_row_ids(rows_per_req, tail_len):
+    """Row ids of the last tail_len[j] rows of every request j, in row order."""
+    out, start = [], 0
+    for n, t in zip(rows_per_req, tail_len):
+        out.extend(range(start + int(n) - int(t), start + int(n)))
+        start += int(n)
+    return np.asarray(out, dtype=np.int64)
 
 
 class Chunk:
@@ -61,7 +96,7 @@ class Chunk:
 
     def __init__(self, wl, device="cuda", n_consumers=None, k_source=None, with_offset=True,
                  share_T=True, fused_keys=True, consumer_bf16=False, overlap_selects=None,
-                 source_side=True):
+                 source_side=True, tail_layers=0):
         self.wl = wl
         self.fused_keys = fused_keys
         self.consumer_bf16 = consumer_bf16   # consumers write and select bf16 scores
@@ -84,8 +119,27 @@ class Chunk:
         tdt = torch.bfloat16 if consumer_bf16 else torch.float32
         self.T = [torch.empty((self.R, self.kb * 8), dtype=tdt, device=device) for _ in range(nT)]
         self.src_top = torch.empty((self.R, self.k_src), dtype=torch.int32, device=device)
-        self.cons_top = [torch.empty((self.R, self.kc), dtype=torch.int32, device=device)
-                         for _ in range(ncons)]
+        # the last tail_layers consumers see only each request's tail rows
+        if tail_layers and wl.tail_len is None:
+            raise ValueError("tail_layers needs a workload with tail lengths")
+        self.n_tail_layers = min(int(tail_layers), ncons)
+        self.tail = None
+        if self.n_tail_layers:
+            trows = tail_row_ids(wl.rows_per_req, wl.tail_len)
+            self.tail_rows = trows
+            self.tail_rpr = _dev(wl.rows_per_req, torch.int32, device)
+            self.tail_len = _dev(wl.tail_len, torch.int32, device)
+            self.tail = Table(len(trows), self.kb, device)
+            self.tail_ws = tail_workspace(len(wl.rows_per_req), device)
+            self.tail_off = _dev(wl.req_start[trows], torch.int32, device) if with_offset else None
+            for i in range(ncons - self.n_tail_layers, ncons):   # those layers' tail-row queries
+                L = layers[1 + i]
+                self.queries[1 + i] = Query(_dev(L.qv[trows], torch.uint8, device),
+                                            _dev(L.qs[trows], torch.uint8, device),
+                                            _dev(L.w[trows], torch.float32, device))
+            self.T_tail = torch.empty((len(trows), self.kb * 8), dtype=tdt, device=device)
+        self.cons_top = [torch.empty((self.R if not self._is_tail(i) else len(self.tail_rows), self.kc),
+                                     dtype=torch.int32, device=device) for i in range(ncons)]
         self.ws = score_workspace(self.R, device)      # folded queries of the layer being scored
         self.side = torch.cuda.Stream(device=device)
         self.scores_ready = torch.cuda.Event()
@@ -96,6 +150,9 @@ class Chunk:
         self.select_done = [torch.cuda.Event() for _ in range(ncons)]
         self.recorder = None     # optional: object with mark(name) (timing only)
         self.graph = None        # run() captured by capture()
+
+    def _is_tail(self, i: int) -> bool:
+        return i >= len(self.queries) - 1 - self.n_tail_layers
 
     def _mark(self, name: str):
         if self.recorder is not None:
@@ -120,7 +177,10 @@ class Chunk:
             for t in (self.S, self.keys, *self.table.tensors(), self.rows.req, self.rows.len,
                       self.src_top, *((self.rows.pos_offset,) if self.rows.pos_offset is not None else ())):
                 t.record_stream(self.side)
-        with torch.cuda.stream(self.side):
+            if self.tail is not None:
+                for t in (*self.tail.tensors(), self.tail_rpr, self.tail_len, self.tail_ws):
+                    t.record_stream(self.side)
+        with _forked(self.side, main):
             if not self.fused_keys:
                 self._mark("amax8<")
                 idx_amax8_varlen(self.S, self.rows.len, self.keys, skip_le_blocks=self.kb)
@@ -130,11 +190,18 @@ class Chunk:
             self._mark("topk_blocks>")
             idx_expand_candidates(self.kp, self.rows, self.table)   # records table.ready
             self._mark("expand>")
+            if self.tail is not None:   # records tail.ready; same stream as the table
+                idx_prefill_tail(self.table, self.tail_rpr, self.tail_len, self.tail, ws=self.tail_ws,
+                                 wait_full=False)
+                self._mark("tail>")
 
-    def source_topk(self):
-        """The source's own top-k (waits for the table when it reads it)."""
+    def source_topk(self, same_stream_as_table=False):
+        """The source's own top-k (waits for the table when it reads it, unless it
+        runs on the stream that built the table: a stream never waits on an event
+        it recorded itself, which a graph capture cannot express)."""
         if self.kb >= self.k_src + 1:
-            stream_wait_table(self.table)
+            if not same_stream_as_table:
+                stream_wait_table(self.table)
             self._mark("source_topk<")
             idx_topk_rows(self.S, self.table.valid_len, self.k_src, self.src_top, mode=COLS_GATHER,
                           blocks=self.table.blocks, pos_offset=self.rows.pos_offset)
@@ -145,17 +212,25 @@ class Chunk:
         self._mark("source_topk>")
 
     # -- a consumer layer ---------------------------------------------------
+    def _layer_table(self, i: int):
+        """(table, row offsets, score buffer or None) of consumer i."""
+        if self._is_tail(i):
+            return self.tail, self.tail_off, self.T_tail
+        return self.table, self.rows.pos_offset, None
+
     def _score(self, i: int, T):
         score = idx_score_sparse_paged_bf16 if self.consumer_bf16 else idx_score_sparse_paged
+        tbl, _, T_own = self._layer_table(i)
         self._mark(f"sparse{i}<")
-        score(self.queries[1 + i], self.kp, self.table, T, ws=self.ws)
+        score(self.queries[1 + i], self.kp, tbl, T if T_own is None else T_own, ws=self.ws)
         self._mark(f"sparse{i}>")
 
     def _select(self, i: int, T):
         select = idx_topk_rows_bf16 if self.consumer_bf16 else idx_topk_rows
+        tbl, off, T_own = self._layer_table(i)
         self._mark(f"topk_rows{i}<")
-        select(T, self.table.valid_len, self.kc, self.cons_top[i], mode=COLS_BLOCKMAP,
-               blocks=self.table.blocks, pos_offset=self.rows.pos_offset)
+        select(T if T_own is None else T_own, tbl.valid_len, self.kc, self.cons_top[i],
+               mode=COLS_BLOCKMAP, blocks=tbl.blocks, pos_offset=off)
         self._mark(f"topk_rows{i}>")
 
     def consumer(self, i: int):
@@ -167,16 +242,25 @@ class Chunk:
         """source + publish + source top-k + every consumer, on the current stream
         (the selects on their own stream when overlap is on; the current stream
         waits for them before returning)."""
+        main = torch.cuda.current_stream()
         self.score_source()
         self.publish()
+        try:
+            self._run_layers(main)
+        finally:
+            # every fork is joined, also when a call raised
+            main.wait_stream(self.side)
+            if self.sel is not None:
+                main.wait_stream(self.sel)
+
+    def _run_layers(self, main):
         if not self.overlap:
             if self.source_side:
                 # the source's own top-k (HBM-bound: it gathers S at the
                 # candidates) behind the expansion on the side stream, beside
                 # the first consumer's scores (MFMA/VALU-bound)
-                main = torch.cuda.current_stream()
-                with torch.cuda.stream(self.side):
-                    self.source_topk()
+                with _forked(self.side, main):
+                    self.source_topk(same_stream_as_table=True)
                     self.source_done.record(self.side)
                 for i in range(len(self.cons_top)):
                     self.consumer(i)
@@ -186,8 +270,7 @@ class Chunk:
             for i in range(len(self.cons_top)):
                 self.consumer(i)
             return
-        main = torch.cuda.current_stream()
-        with torch.cuda.stream(self.sel):
+        with _forked(self.sel, main):
             self.sel.wait_event(self.scores_ready)
             self.source_topk()
         nT = len(self.T)
@@ -197,11 +280,10 @@ class Chunk:
                 main.wait_event(self.select_done[i - nT])   # the select that last read T
             self._score(i, T)
             self.sparse_done[i].record(main)
-            with torch.cuda.stream(self.sel):
+            with _forked(self.sel, main):
                 self.sel.wait_event(self.sparse_done[i])
                 self._select(i, T)
                 self.select_done[i].record(self.sel)
-        main.wait_stream(self.sel)
 
     # -- run() as one HIP graph ------------------------------------------------
     def capture(self):

@@ -1,4 +1,4 @@
-// Candidate expansion, the sparse scorer's work list and the tail-row gather.
+// Candidate expansion, the sparse scorer's work list and the tail rows.
 //
 // idx_expand_candidates (sglang PR "[DSv4.1] Score prefill consumer index
 // layers on candidate blocks with DeepGEMM", Design, "Level one": the pool
@@ -64,8 +64,66 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
   sched[5 + 2 * e] = u * kUnitBlocks < nk ? u * kUnitBlocks : -1;
 }
 
+// Tail row list on the device (so that the tail step never waits on the host
+// and can be captured into a graph).  One workgroup walks the requests in
+// slices of 1024 with a block-wide scan and writes, per request j,
+//   ts[j]  = first tail row of j = sum_{i<j} t_i   (ts[num_req] = all tail rows)
+//   src[j] = first source row of j's tail = sum_{i<j} n_i + n_j - t_j
+// with n_j = max(rows_per_req[j], 0) and t_j clamped into [0, n_j].
+constexpr int kTailScanThreads = 1024;
+
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < kTailScanThreads / 64; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  __syncthreads();   // wsum is reused by the next scan
+  *total = tot;
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kTailScanThreads) void tail_index_kernel(
+    const int32_t* __restrict__ rows_per_req, const int32_t* __restrict__ tail_len, int num_req,
+    int32_t* __restrict__ ts, int32_t* __restrict__ src) {
+  __shared__ int wsum[kTailScanThreads / 64];
+  int carry_t = 0, carry_n = 0;
+  for (int base = 0; base < num_req; base += kTailScanThreads) {
+    const int j = base + (int)threadIdx.x;
+    int n = 0, t = 0;
+    if (j < num_req) {
+      n = max(rows_per_req[j], 0);
+      t = min(max(tail_len[j], 0), n);
+    }
+    int tot_t, tot_n;
+    const int et = block_excl_scan(t, wsum, &tot_t);
+    const int en = block_excl_scan(n, wsum, &tot_n);
+    if (j < num_req) {
+      ts[j] = carry_t + et;
+      src[j] = carry_n + en + n - t;
+    }
+    carry_t += tot_t;
+    carry_n += tot_n;
+  }
+  if (threadIdx.x == 0) ts[num_req] = carry_t;
+}
+
+// Tail row t copies source row src[j] + (t - ts[j]) of the request j whose tail
+// holds it (the last j with ts[j] <= t); rows past ts[num_req] (a tail table
+// larger than the tail lengths say) are written empty, and source rows are
+// clamped into the full table.
 __global__ __launch_bounds__(256) void tail_gather_kernel(
-    const int32_t* __restrict__ src_rows, int kb, const int32_t* __restrict__ blocks,
+    const int32_t* __restrict__ ts, const int32_t* __restrict__ src, int num_req, int full_rows,
+    int kb, const int32_t* __restrict__ blocks,
     const int32_t* __restrict__ n_kept, const int32_t* __restrict__ phys,
     const int32_t* __restrict__ valid_len, const int32_t* __restrict__ len,
     const int32_t* __restrict__ req, int32_t* __restrict__ t_blocks, int32_t* __restrict__ t_n_kept,
@@ -73,16 +131,24 @@ __global__ __launch_bounds__(256) void tail_gather_kernel(
     int32_t* __restrict__ t_req, int chunks) {
   const int t = blockIdx.x / chunks;
   const int i = (blockIdx.x % chunks) * 256 + threadIdx.x;
-  const int s = src_rows[t];
+  int s = -1;
+  if (full_rows > 0 && t < ts[num_req]) {
+    int lo = 0, hi = num_req;   // ts[lo] <= t < ts[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ts[mid] <= t) lo = mid; else hi = mid;
+    }
+    s = min(max(src[lo] + (t - ts[lo]), 0), full_rows - 1);
+  }
   if (i < kb) {
-    t_blocks[(int64_t)t * kb + i] = blocks[(int64_t)s * kb + i];
-    t_phys[(int64_t)t * kb + i] = phys[(int64_t)s * kb + i];
+    t_blocks[(int64_t)t * kb + i] = s >= 0 ? blocks[(int64_t)s * kb + i] : 0x7fffffff;
+    t_phys[(int64_t)t * kb + i] = s >= 0 ? phys[(int64_t)s * kb + i] : -1;
   }
   if (i == 0) {
-    t_n_kept[t] = n_kept[s];
-    t_valid_len[t] = valid_len[s];
-    t_len[t] = len[s];
-    t_req[t] = req[s];
+    t_n_kept[t] = s >= 0 ? n_kept[s] : 0;
+    t_valid_len[t] = s >= 0 ? valid_len[s] : 0;
+    t_len[t] = s >= 0 ? len[s] : 0;
+    t_req[t] = s >= 0 ? req[s] : 0;
   }
 }
 
@@ -116,19 +182,30 @@ hipError_t launch_expand(const PoolArgs& kp, const int32_t* req, const int32_t* 
   return launch_schedule(n_kept, rows, kb, schedule, st);
 }
 
-hipError_t launch_tail_gather(const int32_t* src_rows, int tail_rows, int kb,
-                              const int32_t* blocks, const int32_t* n_kept, const int32_t* phys,
-                              const int32_t* valid_len, const int32_t* len, const int32_t* req,
-                              int32_t* t_blocks, int32_t* t_n_kept, int32_t* t_phys,
-                              int32_t* t_valid_len, int32_t* t_len, int32_t* t_req,
-                              hipStream_t st) {
+size_t tail_workspace_bytes(int num_req) {
+  const size_t n = (size_t)(num_req > 0 ? num_req : 0);
+  return ((2 * n + 1) * sizeof(int32_t) + 15) / 16 * 16;
+}
+
+hipError_t launch_tail(const int32_t* rows_per_req, const int32_t* tail_len, int num_req,
+                       void* ws, int full_rows, int tail_rows, int kb, const int32_t* blocks,
+                       const int32_t* n_kept, const int32_t* phys, const int32_t* valid_len,
+                       const int32_t* len, const int32_t* req, int32_t* t_blocks,
+                       int32_t* t_n_kept, int32_t* t_phys, int32_t* t_valid_len, int32_t* t_len,
+                       int32_t* t_req, hipStream_t st) {
   if (tail_rows <= 0) return hipSuccess;
+  int32_t* ts = static_cast<int32_t*>(ws);
+  int32_t* src = ts + (num_req > 0 ? num_req : 0) + 1;
+  hipLaunchKernelGGL(tail_index_kernel, dim3(1), dim3(kTailScanThreads), 0, st, rows_per_req,
+                     tail_len, num_req, ts, src);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int chunks = (kb + 255) / 256;
   const int64_t grid = (int64_t)tail_rows * chunks;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(tail_gather_kernel, dim3((unsigned)grid), dim3(256), 0, st, src_rows, kb,
-                     blocks, n_kept, phys, valid_len, len, req, t_blocks, t_n_kept, t_phys,
-                     t_valid_len, t_len, t_req, chunks);
+  hipLaunchKernelGGL(tail_gather_kernel, dim3((unsigned)grid), dim3(256), 0, st, ts, src, num_req,
+                     full_rows, kb, blocks, n_kept, phys, valid_len, len, req, t_blocks, t_n_kept,
+                     t_phys, t_valid_len, t_len, t_req, chunks);
   return hipGetLastError();
 }
 

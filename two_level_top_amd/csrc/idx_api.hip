@@ -4,8 +4,6 @@
 #include <stdio.h>
 #include <string.h>
 
-#include <vector>
-
 #include "idx.h"
 #include "idx_internal.h"
 
@@ -118,7 +116,7 @@ size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k) {
     case IDX_OP_SCHEDULE:
       return idxk::schedule_bytes(rows, (int)width);
     case IDX_OP_TAIL:
-      return (size_t)(rows > 0 ? rows : 0) * sizeof(int32_t);
+      return idxk::tail_workspace_bytes(rows);
     case IDX_OP_SCORE:
       return (size_t)(rows > 0 ? rows : 0) * idxk::kFoldRowBytes;
     default:
@@ -329,48 +327,34 @@ idx_status idx_topk_rows_bf16(const uint16_t* X, int64_t ld, const int32_t* vali
                         "idx_topk_rows_bf16");
 }
 
-idx_status idx_prefill_tail(const idx_table* full, const int32_t* rows_per_req_host,
-                            const int32_t* tail_len_host, int32_t num_req, idx_table* tail,
-                            void* ws, size_t ws_bytes, hipStream_t stream) {
+idx_status idx_prefill_tail(const idx_table* full, const int32_t* rows_per_req,
+                            const int32_t* tail_len, int32_t num_req, idx_table* tail, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   const char* fn = "idx_prefill_tail";
   TRY(check_table(full, fn, false));
   TRY(check_table(tail, fn, true));
   if (num_req < 0) return fail(IDX_E_ARG, "%s: num_req < 0", fn);
-  if (num_req > 0 && (!rows_per_req_host || !tail_len_host))
-    return fail(IDX_E_ARG, "%s: rows_per_req_host/tail_len_host is NULL", fn);
+  if (num_req > 0 && (!rows_per_req || !tail_len))
+    return fail(IDX_E_ARG, "%s: rows_per_req/tail_len is NULL", fn);
   if (full->kb != tail->kb) return fail(IDX_E_SHAPE, "%s: kb %d != %d", fn, full->kb, tail->kb);
-  std::vector<int32_t> src;
-  int64_t start = 0;
-  for (int j = 0; j < num_req; ++j) {
-    const int32_t n = rows_per_req_host[j], t = tail_len_host[j];
-    if (n < 0 || t < 0 || t > n)
-      return fail(IDX_E_ARG, "%s: request %d has rows %d, tail %d", fn, j, n, t);
-    for (int32_t i = n - t; i < n; ++i) src.push_back((int32_t)(start + i));
-    start += n;
+  if (tail->rows > 0 && (full->rows == 0 || num_req == 0))
+    return fail(IDX_E_SHAPE, "%s: %d tail rows from a table of %d rows and %d requests", fn,
+                tail->rows, full->rows, num_req);
+  const size_t need = idxk::tail_workspace_bytes(num_req);
+  if (tail->rows > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(IDX_E_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws ? ws_bytes : (size_t)0, need);
+    if (!aligned(ws, 4)) return fail(IDX_E_ALIGN, "%s: workspace must be 4-byte aligned", fn);
   }
-  if (start != full->rows)
-    return fail(IDX_E_SHAPE, "%s: rows_per_req sums to %lld, table has %d rows", fn, (long long)start, full->rows);
-  if ((int64_t)src.size() != tail->rows)
-    return fail(IDX_E_SHAPE, "%s: tail lengths sum to %zu, tail table has %d rows", fn, src.size(), tail->rows);
-  const size_t need = src.size() * sizeof(int32_t);
-  if (need > 0 && (!ws || ws_bytes < need))
-    return fail(IDX_E_WORKSPACE, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
   hipError_t e = hipSuccess;
   if (full->ready) {
     e = hipStreamWaitEvent(stream, full->ready, 0);
     if (e != hipSuccess) return hip_status(e, "idx_prefill_tail: hipStreamWaitEvent");
   }
-  if (need > 0) {
-    e = hipMemcpyAsync(ws, src.data(), need, hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return hip_status(e, "idx_prefill_tail: hipMemcpyAsync");
-    // the host vector dies with this call: make sure the copy has read it
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_status(e, "idx_prefill_tail: hipStreamSynchronize");
-  }
-  e = idxk::launch_tail_gather(static_cast<const int32_t*>(ws), tail->rows, tail->kb, full->blocks,
-                               full->n_kept, full->phys, full->valid_len, full->len, full->req,
-                               tail->blocks, tail->n_kept, tail->phys, tail->valid_len, tail->len,
-                               tail->req, stream);
+  e = idxk::launch_tail(rows_per_req, tail_len, num_req, ws, full->rows, tail->rows, tail->kb,
+                        full->blocks, full->n_kept, full->phys, full->valid_len, full->len,
+                        full->req, tail->blocks, tail->n_kept, tail->phys, tail->valid_len,
+                        tail->len, tail->req, stream);
   if (e != hipSuccess) return hip_status(e, fn);
   e = idxk::launch_schedule(tail->n_kept, tail->rows, tail->kb, tail->schedule, stream);
   if (e != hipSuccess) return hip_status(e, fn);

@@ -75,12 +75,14 @@ hipError_t launch_score_sparse(const QueryArgs& q, const uint8_t* fold, const ui
                                const int32_t* valid_len, int rows, int kb, const void* schedule,
                                void* T, int64_t ld, bool bf16, hipStream_t st);
 
-hipError_t launch_tail_gather(const int32_t* src_rows, int tail_rows, int kb,
-                              const int32_t* blocks, const int32_t* n_kept, const int32_t* phys,
-                              const int32_t* valid_len, const int32_t* len, const int32_t* req,
-                              int32_t* t_blocks, int32_t* t_n_kept, int32_t* t_phys,
-                              int32_t* t_valid_len, int32_t* t_len, int32_t* t_req,
-                              hipStream_t st);
+// the tail table of idx_prefill_tail; ws: tail_workspace_bytes(num_req)
+hipError_t launch_tail(const int32_t* rows_per_req, const int32_t* tail_len, int num_req,
+                       void* ws, int full_rows, int tail_rows, int kb, const int32_t* blocks,
+                       const int32_t* n_kept, const int32_t* phys, const int32_t* valid_len,
+                       const int32_t* len, const int32_t* req, int32_t* t_blocks,
+                       int32_t* t_n_kept, int32_t* t_phys, int32_t* t_valid_len, int32_t* t_len,
+                       int32_t* t_req, hipStream_t st);
+size_t tail_workspace_bytes(int num_req);
 
 size_t schedule_bytes(int rows, int kb);
 hipError_t launch_q_rope_quant(const uint16_t* q, const int32_t* positions, const float* cos_sin,

@@ -249,6 +249,16 @@ def decode(keep_keys: bool = False, n_consumers: int = 4) -> Workload:
                      1 + n_consumers, keep_keys=keep_keys)
 
 
+def decode_mtp(keep_keys: bool = False, n_consumers: int = 4, next_n: int = 2) -> Workload:
+    """Decode with multi-token prediction / verification: 64 requests x next_n
+    rows, the rows of a request seeing contexts C - next_n + 1 .. C (C - 1 and C
+    for next_n = 2), C ~ U{4096..65536}, H=64."""
+    ctx = _rng(6, 0, _T_LEN).integers(4096, 65536, size=64, endpoint=True)
+    lens = [c - next_n + 1 + np.arange(next_n) for c in ctx]
+    return _assemble("decode_mtp", 6, 64, 2048, 512, ctx, [next_n] * 64, lens, False,
+                     1 + n_consumers, keep_keys=keep_keys)
+
+
 def prefill(keep_keys: bool = False, n_consumers: int = 4) -> Workload:
     """1 request, 2048 rows ending at context 65536 (len = 63488 + i), H=64."""
     R, C = 2048, 65536
@@ -289,7 +299,20 @@ def custom(name: str, cfg: int, heads: int, kb: int, kc: int, ctx, rows_per_req,
                      n_layers, dup_frac=dup_frac, tail=tail, keep_keys=keep_keys)
 
 
-CONFIGS = {"tiny": tiny, "decode": decode, "prefill": prefill, "long": long_chunk, "mixed": mixed}
+CONFIGS = {"tiny": tiny, "decode": decode, "decode_mtp": decode_mtp, "prefill": prefill,
+           "long": long_chunk, "mixed": mixed}
+
+
+def select_rows(wl: Workload, idx) -> Workload:
+    """The workload restricted to rows `idx` (same pool, page table and requests;
+    each layer's query rows sliced), e.g. to score rows apart from their batch."""
+    idx = np.asarray(idx, dtype=np.int64)
+    layers = [Layer(L.qv[idx], L.qs[idx], L.w[idx]) for L in wl.layers]
+    rows_per_req = np.bincount(wl.req[idx], minlength=wl.num_req).astype(np.int32)
+    return Workload(name=wl.name + "_rows", cfg=wl.cfg, heads=wl.heads, kb=wl.kb, kc=wl.kc,
+                    ctx=wl.ctx, rows_per_req=rows_per_req, req=wl.req[idx], lens=wl.lens[idx],
+                    req_start=wl.req_start[idx], pool=wl.pool, page_table=wl.page_table,
+                    layers=layers, tail_len=None)
 
 
 # ---------------------------------------------------------------------------
