@@ -277,6 +277,26 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
                                   hipStream_t stream);
 
 /*
+ * idx_score_sparse_paged_noalloc -- idx_score_sparse_paged for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same kernels, with the folded
+ * queries in a scratch array inside the library instead of a workspace
+ * argument.  Same arguments, results (bit for bit) and errors otherwise.
+ *   q->rows <= 4096 (else IDX_E_UNSUPPORTED, nothing enqueued): the scratch
+ *   holds 4096 rows x 1088 bytes (4.25 MiB), one copy per GPU, held until
+ *   the process ends.
+ * The first call on a device looks the scratch address up with that device
+ * current (make that first call outside a graph capture).  Every call on a
+ * GPU shares that GPU's scratch, which keeps the last call's contents (each
+ * call overwrites the rows it reads; nothing needs clearing): calls that
+ * overlap on one GPU -- on different streams, or in graphs replayed
+ * concurrently -- race, so the caller orders them.
+ */
+idx_status idx_score_sparse_paged_noalloc(const idx_query* q, const idx_kpool* kp,
+                                          const idx_table* tbl, float* T, int64_t ld,
+                                          hipStream_t stream);
+
+/*
  * idx_score_sparse_paged_bf16 -- the same scores written as bf16 (the
  * prefill PR's consumer output, "Level two": bf16 [tokens, 2048 x 8]): each
  * element is the fp32 score of idx_score_sparse_paged rounded to the nearest

@@ -175,6 +175,15 @@ def test_library_never_synchronises():
             assert call not in text, f"{name} calls {call}"
 
 
+def test_noalloc_rejects_rows_above_its_scratch(lib):
+    t, q, kp, rows, tbl = _structs()
+    P = ctypes.byref
+    big = t._Query(FAKE, FAKE, FAKE, 4097, 64, 128)
+    assert lib.idx_score_sparse_paged_noalloc(P(big), P(kp), P(tbl), FAKE, 1 << 14, None) == -4
+    assert "4096" in _err(lib)
+    assert lib.idx_score_sparse_paged_noalloc(None, P(kp), P(tbl), FAKE, 1 << 14, None) == -1
+
+
 def test_workspace_sizes(lib):
     assert lib.idx_workspace_bytes(3, 16384, 2048, 0) == 16 + 16384 * 32 * 8
     assert lib.idx_workspace_bytes(4, 100, 0, 0) == (2 * 100 + 1) * 4 + 12   # 16-byte multiple

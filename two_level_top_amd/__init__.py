@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "IdxError", "Query", "KPool", "Rows", "Table", "load",
     "idx_score_dense", "idx_score_dense_keys", "idx_q_rope_quant", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
-    "idx_score_sparse_paged", "idx_score_sparse_paged_bf16", "idx_topk_rows", "idx_topk_rows_bf16",
+    "idx_score_sparse_paged", "idx_score_sparse_paged_bf16", "idx_score_sparse_paged_noalloc",
+    "idx_topk_rows", "idx_topk_rows_bf16",
     "idx_prefill_tail", "idx_workspace_bytes",
     "COLS_IDENTITY", "COLS_BLOCKMAP", "COLS_GATHER", "stream_wait_table", "score_workspace",
     "tail_workspace",
@@ -91,6 +92,7 @@ def load():
         "idx_topk_rows_bf16": [_P, _I64, _P, _I32, _I32, ctypes.c_int, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
         "idx_score_sparse_paged_bf16": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_prefill_tail": [ctypes.POINTER(_Table), _P, _P, _I32, ctypes.POINTER(_Table), _P, ctypes.c_size_t, _P],
+        "idx_score_sparse_paged_noalloc": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -402,6 +404,17 @@ def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=
                                          _ptr(T), T.stride(0), _ptr(ws), ws.numel(),
                                          _stream(stream)),
            "idx_score_sparse_paged")
+
+
+def idx_score_sparse_paged_noalloc(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, stream=None):
+    """idx_score_sparse_paged with the folded queries in the library's static scratch
+    (at most 4096 query rows): allocates nothing."""
+    _sparse_args(q, tbl, T, torch.float32)
+    q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
+    _check(load().idx_score_sparse_paged_noalloc(ctypes.byref(q_c), ctypes.byref(kp_c),
+                                                 ctypes.byref(t_c), _ptr(T), T.stride(0),
+                                                 _stream(stream)),
+           "idx_score_sparse_paged_noalloc")
 
 
 def idx_score_sparse_paged_bf16(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=None,

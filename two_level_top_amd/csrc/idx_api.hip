@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "idx.h"
 #include "idx_internal.h"
 
@@ -97,6 +99,46 @@ idx_status check_table(const idx_table* t, const char* fn, bool need_schedule) {
     idx_status s_ = (x);             \
     if (s_ != IDX_OK) return s_;     \
   } while (0)
+
+}  // namespace
+
+namespace idxk {
+
+// Scratch of idx_score_sparse_paged_noalloc: the folded queries of up to
+// kNoAllocMaxRows query rows, kFoldRowBytes each (4.25 MiB).  Every GPU the
+// library runs on holds its own copy until the process ends.  Host code never
+// uses this name as an address: the device address comes from
+// hipGetSymbolAddress, once per device (scratch_address below).
+constexpr int kNoAllocMaxRows = 4096;
+__device__ __align__(256) uint8_t scratch[(size_t)kNoAllocMaxRows * kFoldRowBytes];
+
+}  // namespace idxk
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of idxk::scratch, per device
+
+// The current device's address of idxk::scratch (looked up on the first call
+// on that device, with that device current).
+idx_status scratch_address(void** out, const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(IDX_E_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(idxk::scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress of the scratch array");
+    if (!p) return fail(IDX_E_HIP, "%s: hipGetSymbolAddress gave a null scratch address", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return IDX_OK;
+}
 
 }  // namespace
 
@@ -276,6 +318,19 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
                                   float* T, int64_t ld, void* ws, size_t ws_bytes,
                                   hipStream_t stream) {
   return score_sparse_impl(q, kp, tbl, T, ld, false, ws, ws_bytes, stream, "idx_score_sparse_paged");
+}
+
+idx_status idx_score_sparse_paged_noalloc(const idx_query* q, const idx_kpool* kp,
+                                          const idx_table* tbl, float* T, int64_t ld,
+                                          hipStream_t stream) {
+  const char* fn = "idx_score_sparse_paged_noalloc";
+  if (!q) return fail(IDX_E_ARG, "%s: query is NULL", fn);
+  if (q->rows > idxk::kNoAllocMaxRows)
+    return fail(IDX_E_UNSUPPORTED, "%s: %d query rows above the %d rows of the static scratch", fn,
+                q->rows, idxk::kNoAllocMaxRows);
+  void* ws = nullptr;
+  if (q->rows > 0) TRY(scratch_address(&ws, fn));
+  return score_sparse_impl(q, kp, tbl, T, ld, false, ws, sizeof(idxk::scratch), stream, fn);
 }
 
 idx_status idx_score_sparse_paged_bf16(const idx_query* q, const idx_kpool* kp, const idx_table* tbl,
