@@ -73,18 +73,25 @@ __device__ __forceinline__ float max8_lanes(float v) {
   return c;
 }
 
-// K operands of one pool page: 4 MFMA tiles of 16 positions.
+// K operands of one pool page: the values of its 4 MFMA tiles of 16
+// positions, and its 256 scale bytes in one register (lane l: the 4 scale
+// bytes of position l), fetched with one 4-byte load per lane instead of one
+// 64-lane byte load per tile.
 struct PageOps {
   uint4 b[4];
-  int sb[4];
+  uint32_t s;
 };
 
 __device__ __forceinline__ void load_page(__amdgpu_buffer_rsrc_t pg, uint32_t voff, uint32_t soff, PageOps& o) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    o.b[t] = buffer_load_b128(pg, voff + t * 16 * kValBytes);
-    o.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(pg, soff + t * 16 * kScaleBytes, 0, 0);
-  }
+  for (int t = 0; t < 4; ++t) o.b[t] = buffer_load_b128(pg, voff + t * 16 * kValBytes);
+  o.s = __builtin_amdgcn_raw_buffer_load_b32(pg, soff, 0, 0);
+}
+
+// tile t's scale for this lane: byte l / 16 of position 16 t + l % 16's scales
+// (the MFMA reads the low byte)
+__device__ __forceinline__ int page_tile_scale(const PageOps& o, int t, int sdist, uint32_t sshift) {
+  return (int)((uint32_t)__builtin_amdgcn_ds_bpermute(sdist + 64 * t, (int)o.s) >> sshift);
 }
 
 // Score NR (1 or 2) rows of one request against positions [c0, cend) (c0 on
@@ -99,7 +106,9 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* con
                                            int num_pages, const int32_t* pt, int max_pages,
                                            int c0, int cend, int lane) {
   const uint32_t voff = (uint32_t)((lane & 15) * kValBytes + (lane >> 4) * 16);
-  const uint32_t soff = (uint32_t)(kPageValBytes + (lane & 15) * kScaleBytes + (lane >> 4));
+  const uint32_t soff = (uint32_t)(kPageValBytes + lane * kScaleBytes);   // position l's scales
+  const int sdist = 4 * (lane & 15);
+  const uint32_t sshift = 8u * (uint32_t)(lane >> 4);
   const int npg = (cend - c0 + kPage - 1) / kPage;
   const int pid = (int)clamp_page(pt[min(c0 / kPage + min(lane, npg - 1), max_pages - 1)], num_pages);
   auto load = [&](int i, PageOps& o) {
@@ -116,10 +125,11 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* con
     float part[NR][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      const int sb = page_tile_scale(cur, t, sdist, sshift);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         v4f acc[HB + 1];
-        tile_mfma<HB>(f[r], cur.b[t], cur.sb[t], acc);
+        tile_mfma<HB>(f[r], cur.b[t], sb, acc);
         part[r][t] = tile_epilogue<HB>(f[r], acc);
       }
     }

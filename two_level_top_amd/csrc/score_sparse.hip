@@ -33,29 +33,42 @@ constexpr int kMaxUnitsPerWave = 8;
 // (measured 2.13 -> 2.10 ms per call on the long chunk)
 constexpr int kStoreNT = 2;
 
-// K operands of 4 tiles (8 candidate blocks) of one unit.
+// K operands of 4 tiles (8 candidate blocks) of one unit: each tile's values,
+// and the scales of all 8 blocks in one register -- lane l holds the 4 scale
+// bytes (one per 32-element group) of position l % 8 of block l / 8.  One
+// 4-byte load per lane fetches the group's 256 scale bytes; loading them per
+// tile took four 64-lane byte loads, which cost about as much as the value
+// loads themselves (long chunk: 2.07 ms per call with them, 1.66 ms without).
 struct GroupOps {
   uint4 b[4];
-  int sb[4];
+  uint32_t s;
 };
 
 // Lane l of tile t of group g needs position (l % 8) of candidate block
-// 8 g + 2 t + (l / 8) % 2, 16 bytes at (l / 16) * 16 of its values and byte
+// 8 g + 2 t + (l / 8) % 2: 16 bytes at (l / 16) * 16 of its values, and byte
 // l / 16 of its scales.  The unit's block byte offsets sit one per lane in
 // `bov` (values) and `sov` (scales); ds_bpermute hands each lane its block's
-// pair (the tile's block index is the instruction's immediate offset), so
+// offset (the tile's block index is the instruction's immediate offset), so
 // addressing costs one add per operand.  Blocks past the unit's end repeat
-// its last block and are never stored.
+// its last block (the lanes past it hold the last block's offsets) and are
+// never stored.
 __device__ __forceinline__ void load_group(__amdgpu_buffer_rsrc_t pool, int bov, int sov, int sel,
-                                           uint32_t voff, uint32_t soff, GroupOps& o) {
+                                           int ssel, uint32_t voff, uint32_t soff, GroupOps& o) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int a = sel + 8 * t;   // byte address of the source lane (block 8g + 2t + half)
     const uint32_t vb = (uint32_t)__builtin_amdgcn_ds_bpermute(a, bov);
-    const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(a, sov);
     o.b[t] = buffer_load_b128(pool, vb + voff);
-    o.sb[t] = __builtin_amdgcn_raw_buffer_load_b8(pool, sb + soff, 0, 0);
   }
+  const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(ssel, sov);   // block 8g + l / 8
+  o.s = __builtin_amdgcn_raw_buffer_load_b32(pool, sb + soff, 0, 0);
+}
+
+// tile t's scale for this lane: the dword of lane 16 t + l % 16 (position l % 8
+// of block 2 t + (l / 8) % 2 of the group), byte l / 16 (the MFMA reads the low
+// byte)
+__device__ __forceinline__ int tile_scale(const GroupOps& o, int t, int sdist, uint32_t sshift) {
+  return (int)((uint32_t)__builtin_amdgcn_ds_bpermute(sdist + 64 * t, (int)o.s) >> sshift);
 }
 
 // nearest bf16 of a finite fp32 value (ties to even), as its 16 bits
@@ -82,7 +95,9 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
   const int nunits = min(sched[0], max_units);
   const __amdgpu_buffer_rsrc_t prs = buffer_rsrc(pool, (uint32_t)num_pages * (uint32_t)kPageBytes);
   const uint32_t voff = (uint32_t)((lane & 7) * kValBytes + (lane >> 4) * 16);
-  const uint32_t soff = (uint32_t)((lane & 7) * kScaleBytes + (lane >> 4));
+  const uint32_t soff = (uint32_t)((lane & 7) * kScaleBytes);    // this lane's scale dword
+  const int sdist = 4 * (lane & 15);                             // source lane of tile 0's scale
+  const uint32_t sshift = 8u * (uint32_t)(lane >> 4);            // its byte
   const int half = (lane >> 3) & 1;
   // each wave takes `upw` consecutive units (mostly of one row: the list is
   // row-major) and keeps the row's query in registers across them, or part
@@ -118,12 +133,13 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
                                                    (uint32_t)ncols * kEl);
     const int ngroups = (nblk + 7) / 8;
     auto sel_of = [&](int g) { return 4 * min(8 * g + half, nblk - 1); };
+    auto ssel_of = [&](int g) { return 4 * (8 * g + (lane >> 3)); };
     auto compute = [&](int g, const GroupOps& cur) {
       float p[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         v4f acc[HB + 1];
-        tile_mfma<HB>(f, cur.b[t], cur.sb[t], acc);
+        tile_mfma<HB>(f, cur.b[t], tile_scale(cur, t, sdist, sshift), acc);
         p[t] = tile_epilogue<HB>(f, acc);
       }
       const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
@@ -136,12 +152,14 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
     const int g1 = min(ngroups, g0 + gper);
     if (g0 >= g1) continue;
     GroupOps A, B;
-    load_group(prs, bov, sov, sel_of(g0), voff, soff, A);
+    load_group(prs, bov, sov, sel_of(g0), ssel_of(g0), voff, soff, A);
     for (int g = g0; g < g1; g += 2) {
-      load_group(prs, bov, sov, sel_of(min(g + 1, g1 - 1)), voff, soff, B);
+      const int gb = min(g + 1, g1 - 1);
+      load_group(prs, bov, sov, sel_of(gb), ssel_of(gb), voff, soff, B);
       compute(g, A);
       if (g + 1 >= g1) break;
-      load_group(prs, bov, sov, sel_of(min(g + 2, g1 - 1)), voff, soff, A);
+      const int ga = min(g + 2, g1 - 1);
+      load_group(prs, bov, sov, sel_of(ga), ssel_of(ga), voff, soff, A);
       compute(g + 1, B);
     }
   }
