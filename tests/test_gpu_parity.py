@@ -201,6 +201,11 @@ def test_fold_workspace(idx, name):
     bound = np.repeat(gmax, 32, axis=1) * 3.0 ** -16
     err = np.abs(got - want)
     assert (err <= bound).all(), f"fold residual {err.max():.3g} above the 16-term bound"
+    # the dense scorer uses the first 8 terms (two rows share one MFMA block)
+    got8 = terms[:, :8].sum(axis=1)
+    err8 = np.abs(got8 - want)
+    assert (err8 <= np.repeat(gmax, 32, axis=1) * 3.0 ** -8).all(), \
+        f"8-term fold residual {err8.max():.3g} above its bound"
 
 
 # ---------------------------------------------------------------------------

@@ -37,7 +37,9 @@ struct RowFrag {
   int st;
 };
 
-template <int HB>
+// FOLD: also load the row's own folded-query block (the dense kernel shares
+// one block between two rows instead, see PairFold)
+template <int HB, bool FOLD = true>
 __device__ __forceinline__ void load_row(const QueryArgs& q, const uint8_t* fold, int r, int lane,
                                          RowFrag<HB>& f) {
   const int g = lane >> 4;
@@ -61,9 +63,42 @@ __device__ __forceinline__ void load_row(const QueryArgs& q, const uint8_t* fold
     f.w = (m >> 2) < HB && hw < q.heads ? 0.5f * q.w[(size_t)r * q.heads + hw] : 0.f;
     asm volatile("s_nop 1" : "+v"(f.w));   // VALU write -> DPP read of f.w
   }
+  if (FOLD) {
+    const uint8_t* fr = fold + (size_t)r * kFoldRowBytes;
+    f.at = *reinterpret_cast<const uint4*>(fr + (lane & 15) * kValBytes + g * 16);
+    f.st = fr[kFoldTerms * kValBytes + (lane & 15) * kScaleBytes + g];
+  }
+}
+
+// The folded queries of a pair of rows as one 16-row MFMA block holding the
+// first kPairFoldTerms terms of each row: M row m is term 2 (m / 4) + m % 2 of
+// row (m / 2) % 2 of the pair.  The MFMA then gives the lanes of k-group g the
+// fold values of terms 2g and 2g + 1 of row 0 in outputs 0 and 1 and of row 1
+// in outputs 2 and 3, and the 4-way sum over lane groups adds each row's 8
+// terms.  Eight of the 16 greedy terms leave a fold residual whose effect on a
+// score is below 1e-5 on these inputs (long chunk K, 8.4M scores: at most
+// 4.4e-6); sharing the block saves half an MFMA per tile and row, and two of
+// the epilogue's three adds.  r1 < 0: the second half is zero (one row).
+constexpr int kPairFoldTerms = 8;
+
+struct PairFold {
+  uint4 at;
+  int st;
+};
+
+__device__ __forceinline__ void load_pair_fold(const uint8_t* fold, int r0, int r1, int lane,
+                                               PairFold& p) {
+  const int m = lane & 15, g = lane >> 4;
+  const int r = ((m >> 1) & 1) ? r1 : r0;
+  const int term = 2 * (m >> 2) + (m & 1);
+  if (r < 0) {
+    p.at = make_uint4(0u, 0u, 0u, 0u);
+    p.st = 127;
+    return;
+  }
   const uint8_t* fr = fold + (size_t)r * kFoldRowBytes;
-  f.at = *reinterpret_cast<const uint4*>(fr + (lane & 15) * kValBytes + g * 16);
-  f.st = fr[kFoldTerms * kValBytes + (lane & 15) * kScaleBytes + g];
+  p.at = *reinterpret_cast<const uint4*>(fr + term * kValBytes + g * 16);
+  p.st = fr[kFoldTerms * kValBytes + term * kScaleBytes + g];
 }
 
 // MFMA of query block HBI (scale byte HBI of the packed scales)
@@ -102,6 +137,18 @@ __device__ __forceinline__ void epilogue_blocks(float& s0, float& s1, float& s2,
   }
 }
 
+// two chains: heads 4 hb + {0, 2} into s0, 4 hb + {1, 3} into s1
+template <int HB, int HBI = 0>
+__device__ __forceinline__ void epilogue_pairs(float& s0, float& s1, float w, const v4f (&acc)[HB + 1]) {
+  if constexpr (HBI < HB) {
+    fma_bcast_abs<4 * HBI + 0>(s0, w, acc[HBI + 1][0]);
+    fma_bcast_abs<4 * HBI + 1>(s1, w, acc[HBI + 1][1]);
+    fma_bcast_abs<4 * HBI + 2>(s0, w, acc[HBI + 1][2]);
+    fma_bcast_abs<4 * HBI + 3>(s1, w, acc[HBI + 1][3]);
+    epilogue_pairs<HB, HBI + 1>(s0, s1, w, acc);
+  }
+}
+
 // The HB + 1 MFMAs of one tile (folded block first) ...
 template <int HB>
 __device__ __forceinline__ void tile_mfma(const RowFrag<HB>& f, uint4 b, int sb, v4f (&acc)[HB + 1]) {
@@ -128,6 +175,46 @@ __device__ __forceinline__ void settle(v4f (&acc)[HB + 1]) {
   else
     asm volatile("s_nop 7\n\ts_nop 3"
                  : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]));
+}
+
+// the head blocks' wait states only (acc[0] not read)
+template <int HB>
+__device__ __forceinline__ void settle_heads(v4f (&acc)[HB + 1]) {
+  if constexpr (HB == 1)
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[1]));
+  else if constexpr (HB == 2)
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[1]), "+v"(acc[2]));
+  else if constexpr (HB == 3)
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(acc[4]));
+}
+
+// Epilogue of one row of a pair sharing a fold block.  FIRST (the pair's
+// first row): acc[0] holds the pair's fold outputs; entries 0 and 1 seed this
+// row's two chains, and entries 2 and 3 are handed out in seed0/seed1 for the
+// second row.  Otherwise acc[0] is unused and seed0/seed1 seed the chains.
+// Each chain takes 2 HB FMAs; one add joins them.
+template <int HB, bool FIRST>
+__device__ __forceinline__ float tile_epilogue_pair(const RowFrag<HB>& f, const v4f (&acc_in)[HB + 1],
+                                                    float& seed0, float& seed1) {
+  v4f acc[HB + 1];
+#pragma unroll
+  for (int i = 0; i <= HB; ++i) acc[i] = acc_in[i];
+  float s0, s1;
+  if constexpr (FIRST) {
+    settle<HB>(acc);
+    s0 = acc[0][0];
+    s1 = acc[0][1];
+    seed0 = acc[0][2];
+    seed1 = acc[0][3];
+  } else {
+    settle_heads<HB>(acc);
+    s0 = seed0;
+    s1 = seed1;
+  }
+  epilogue_pairs<HB>(s0, s1, f.w, acc);
+  return s0 + s1;
 }
 
 template <int HB>

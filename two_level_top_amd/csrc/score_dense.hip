@@ -100,7 +100,8 @@ __device__ __forceinline__ int page_tile_scale(const PageOps& o, int t, int sdis
 // the keys of blocks [c0/8, min(cend/8, nblk[r])) (Krow[r] is only used when
 // nblk[r] > 0, i.e. the row is keyed).
 template <int HB, int NR, bool KEYS>
-__device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* const (&Srow)[2],
+__device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const PairFold& pf,
+                                           float* const (&Srow)[2],
                                            const int (&lens)[2], float* const (&Krow)[2],
                                            const int (&nblk)[2], const uint8_t* pool,
                                            int num_pages, const int32_t* pt, int max_pages,
@@ -126,11 +127,19 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], float* con
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int sb = page_tile_scale(cur, t, sdist, sshift);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
+      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+      float seed0, seed1;   // the second row's fold values
+      {
         v4f acc[HB + 1];
-        tile_mfma<HB>(f[r], cur.b[t], sb, acc);
-        part[r][t] = tile_epilogue<HB>(f[r], acc);
+        acc[0] = mfma_fp4_16x16x128(pf.at, cur.b[t], pf.st, sb, zero);   // both rows' folds
+        tile_mfma_blocks<HB>(f[0], cur.b[t], sb, acc);
+        part[0][t] = tile_epilogue_pair<HB, true>(f[0], acc, seed0, seed1);
+      }
+      if (NR == 2) {
+        v4f acc[HB + 1];
+        acc[0] = zero;
+        tile_mfma_blocks<HB>(f[1], cur.b[t], sb, acc);
+        part[NR - 1][t] = tile_epilogue_pair<HB, false>(f[1], acc, seed0, seed1);
       }
     }
     const int p = c0 + i * kPage + lane;
@@ -195,18 +204,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   }
   const int c0 = chunk * chunk_len;
   RowFrag<HB> f[2];
+  PairFold pf;
   float* Srow[2];
   int lens[2];
   if (r1 >= 0 && req1 == req0) {  // both rows read the same keys
     const int cend = min(c0 + chunk_len, max(len0, len1));
     if (c0 >= cend) return;
-    load_row(q, fold, r0, lane, f[0]);
-    load_row(q, fold, r1, lane, f[1]);
+    load_row<HB, false>(q, fold, r0, lane, f[0]);
+    load_row<HB, false>(q, fold, r1, lane, f[1]);
+    load_pair_fold(fold, r0, r1, lane, pf);
     Srow[0] = S + (int64_t)r0 * ld;
     Srow[1] = S + (int64_t)r1 * ld;
     lens[0] = len0;
     lens[1] = len1;
-    score_rows<HB, 2, KEYS>(f, Srow, lens, Krow, nblk, kp.pool, kp.num_pages,
+    score_rows<HB, 2, KEYS>(f, pf, Srow, lens, Krow, nblk, kp.pool, kp.num_pages,
                             kp.page_table + (int64_t)req0 * kp.max_pages, kp.max_pages, c0, cend, lane);
     return;
   }
@@ -217,14 +228,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int rq = i == 0 ? req0 : req1;
     const int cend = min(c0 + chunk_len, L);
     if (c0 >= cend) continue;
-    load_row(q, fold, r, lane, f[0]);
+    load_row<HB, false>(q, fold, r, lane, f[0]);
+    load_pair_fold(fold, r, -1, lane, pf);   // the row in the first half, as in a pair
     Srow[0] = S + (int64_t)r * ld;
     Srow[1] = Srow[0];
     lens[0] = L;
     lens[1] = 0;
     float* const Kr[2] = {Krow[i], Krow[i]};
     const int nb[2] = {nblk[i], 0};
-    score_rows<HB, 1, KEYS>(f, Srow, lens, Kr, nb, kp.pool, kp.num_pages,
+    score_rows<HB, 1, KEYS>(f, pf, Srow, lens, Kr, nb, kp.pool, kp.num_pages,
                             kp.page_table + (int64_t)rq * kp.max_pages, kp.max_pages, c0, cend, lane);
   }
 }
