@@ -116,12 +116,10 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const Pair
     const int64_t pg = __builtin_amdgcn_readlane(pid, min(i, npg - 1));
     load_page(buffer_rsrc(pool + pg * kPageBytes, kPageBytes), voff, soff, o);
   };
-  __amdgpu_buffer_rsrc_t rs[2], rk[2];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    rs[r] = buffer_rsrc(Srow[r], (uint32_t)lens[r] * 4u);
-    if (KEYS) rk[r] = buffer_rsrc(Krow[r], (uint32_t)nblk[r] * 4u);
-  }
+  // per-lane store offsets: score of position l of a page; key of block l / 8
+  // from lanes 8j (the others get an offset past every resource: dropped)
+  const uint32_t soffs = (uint32_t)lane * 4u;
+  const uint32_t koffs = (lane & 7) == 0 ? (uint32_t)(lane >> 3) * 4u : 0x80000000u;
   auto compute = [&](int i, const PageOps& cur) {
     float part[NR][4];
 #pragma unroll
@@ -142,17 +140,23 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const Pair
         part[NR - 1][t] = tile_epilogue_pair<HB, false>(f[1], acc, seed0, seed1);
       }
     }
-    const int p = c0 + i * kPage + lane;
+    // the page's store resources start at its first position (block) and end
+    // at the row's length (keys), so the per-lane offsets stay fixed; these
+    // are scalar operations
+    const int pb0 = c0 + i * kPage;
+    const int kb0 = pb0 / kBlock;
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       const float tot = reduce_scatter4(part[r][0], part[r][1], part[r][2], part[r][3]);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), rs[r], (uint32_t)p * 4u, 0, 0);
+      const uint32_t rem = lens[r] > pb0 ? (uint32_t)(lens[r] - pb0) * 4u : 0u;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), buffer_rsrc(Srow[r] + pb0, rem), soffs, 0, 0);
       if (KEYS) {
-        const float m = max8_lanes(tot);
-        const int blk = p >> 3;
-        const float key = blk == nblk[r] - 1 ? __builtin_inff() : m;
-        const uint32_t koff = (lane & 7) == 0 ? (uint32_t)blk * 4u : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key), rk[r], koff, 0, 0);
+        float key = max8_lanes(tot);
+        const int newest = nblk[r] - 1 - kb0;   // the newest block's index in the page
+        if (newest >= 0 && newest < kBlocksPerPage)   // (uniform) its key is +inf
+          key = (lane >> 3) == newest ? __builtin_inff() : key;
+        const uint32_t krem = nblk[r] > kb0 ? (uint32_t)(nblk[r] - kb0) * 4u : 0u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key), buffer_rsrc(Krow[r] + kb0, krem), koffs, 0, 0);
       }
     }
   };

@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
   const int gper = 8 / split;                      // groups per part
   int cur_row = -1;
   RowFrag<HB> f;
+  PairFold pf;   // the row's fold, first 8 terms (the layout the dense kernel uses)
   for (int u = u0; u < u1; ++u) {
     const int row = __builtin_amdgcn_readfirstlane(sched[4 + 2 * u]);
     const int first = __builtin_amdgcn_readfirstlane(sched[5 + 2 * u]);
@@ -118,7 +119,8 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
     const int nblk = min(kUnitBlocks, nk - first);   // candidate blocks of this unit
     if (nblk <= 0) continue;
     if (row != cur_row) {
-      load_row(q, fold, row, lane, f);
+      load_row<HB, false>(q, fold, row, lane, f);
+      load_pair_fold(fold, row, -1, lane, pf);
       cur_row = row;
     }
     // byte offsets of this lane's candidate block (pools are < 4 GiB here)
@@ -138,9 +140,13 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
       float p[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
+        const int sb = tile_scale(cur, t, sdist, sshift);
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
         v4f acc[HB + 1];
-        tile_mfma<HB>(f, cur.b[t], tile_scale(cur, t, sdist, sshift), acc);
-        p[t] = tile_epilogue<HB>(f, acc);
+        acc[0] = mfma_fp4_16x16x128(pf.at, cur.b[t], pf.st, sb, zero);
+        tile_mfma_blocks<HB>(f, cur.b[t], sb, acc);
+        float unused0, unused1;
+        p[t] = tile_epilogue_pair<HB, true>(f, acc, unused0, unused1);
       }
       const float tot = reduce_scatter4(p[0], p[1], p[2], p[3]);
       if (BF16)
