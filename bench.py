@@ -139,11 +139,17 @@ def time_q_rope_quant(rows, heads, reps=20):
 
 
 def time_amax8(ch, bytes_per_call, reps=5):
-    """idx_amax8_varlen alone on the chunk's own score matrix (the chunk takes the
-    block keys from the fused dense pass instead), timed apart from the chunk."""
+    """idx_amax8_varlen alone on the chunk's source score matrix (the chunk takes
+    the block keys from the fused dense pass and never writes the matrix), timed
+    apart from the chunk: the matrix is scored into a buffer of its own first."""
     import torch
     import two_level_top_amd as t
-    run = lambda: t.idx_amax8_varlen(ch.S, ch.rows.len, ch.keys, skip_le_blocks=ch.kb)
+    S = ch.S
+    if S is None:
+        S = torch.empty((ch.R, ch.ld), dtype=torch.float32, device="cuda")
+        t.idx_score_dense(ch.queries[0], ch.kp, ch.rows, S, ws=ch.ws)
+    keys = torch.empty_like(ch.keys)
+    run = lambda: t.idx_amax8_varlen(S, ch.rows.len, keys, skip_le_blocks=ch.kb)
     run()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -280,7 +286,8 @@ def main():
     t_sp = [avg(f"sparse{i}<", f"sparse{i}>") for i in range(ncons)]
     t_tr = [avg(f"topk_rows{i}<", f"topk_rows{i}>") for i in range(ncons)]
     dense_tflops = work["dense_flops"] / (t_dense * 1e-3) / 1e12
-    dense_name = "score_dense_keys" if ch.fused_keys else "score_dense"
+    dense_name = ("score_dense_keys (keys only)" if ch.rescore else "score_dense_keys") \
+        if ch.fused_keys else "score_dense"
     kernels = {
         dense_name: {"ms": round(t_dense, 4), "TFLOP/s": round(dense_tflops, 1),
                      "frac_fp4_peak": round(dense_tflops / PEAK_FP4_TFLOPS, 4)},
@@ -289,10 +296,13 @@ def main():
         "topk_blocks": {"ms": round(t_tkb, 4),
                         "GB/s": round(work["topk_blocks_bytes"] / (t_tkb * 1e-3) / 1e9, 1)},
         "expand_candidates": {"ms": round(t_exp, 4)},
-        "source_topk_rows": {"ms": round(t_src, 4),
-                             **({"note": "timed in line; the timed steps run it on the side stream "
-                                         "beside the first consumer"}
-                                if ch.source_side and not ch.overlap else {})},
+        ("source_rescore_topk" if ch.rescore else "source_topk_rows"): {
+            "ms": round(t_src, 4),
+            **({"note": "the source query scored at its top-(k+1) candidate blocks, then the "
+                        "block-mapped top-k; on the side stream beside the first consumer's "
+                        "scores (events on that stream include the overlap)"} if ch.rescore else
+               {"note": "timed in line; the timed steps run it on the side stream beside the "
+                        "first consumer"} if ch.source_side and not ch.overlap else {})},
         "score_sparse_paged": {"ms": round(float(np.mean(t_sp)), 4),
                                "TFLOP/s": round(work["sparse_flops"] / (np.mean(t_sp) * 1e-3) / 1e12, 1),
                                "gather GB/s": round(work["sparse_gather_bytes"] / (np.mean(t_sp) * 1e-3) / 1e9, 1)},

@@ -228,6 +228,11 @@ idx_status idx_amax8_varlen(const float* S, int64_t ld, const int32_t* len, int3
  * Arguments and errors: the union of the two calls' (ld % 8 == 0, ldk >= 1,
  * skip_le_blocks >= 0, keys 4-byte aligned and non-NULL); S needs only 4-byte
  * alignment.  Same workspace as idx_score_dense.
+ * S == NULL: keys only -- the scores are computed (in full, as above) but
+ * never written, so the [rows, ld] score matrix need not exist; ld still
+ * bounds the lengths and the key count (ld >= max len, as with S).  The
+ * source's own top-k then comes from rescoring its top-(k + 1) blocks (see
+ * idx_topk_blocks_nested).
  */
 idx_status idx_score_dense_keys(const idx_query* q, const idx_kpool* kp, const idx_rows* rows,
                                 float* S, int64_t ld, float* keys, int64_t ldk,
@@ -246,6 +251,28 @@ idx_status idx_score_dense_keys(const idx_query* q, const idx_kpool* kp, const i
 idx_status idx_topk_blocks(const float* keys, int64_t ldk, const int32_t* len, int32_t rows,
                            int32_t kb, int32_t* blocks, int32_t* n_kept, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * idx_topk_blocks_nested -- idx_topk_blocks plus, nested inside the kb best
+ * blocks, the k2 best (1 <= k2 <= kb <= 4096), by the same rule (if nblk <=
+ * k2: blocks 0 .. nblk-1, else the k2 largest keys, ties to the lower block
+ * id; ascending, INT32_MAX padded; n_kept2 = min(nblk, k2)).
+ *   blocks, n_kept     [rows][kb], [rows]: exactly as idx_topk_blocks
+ *   blocks2, n_kept2   [rows][k2], [rows]
+ * Device precondition: the keys of every row with nblk > k2 are present
+ * (written with skip_le_blocks <= k2); rows with nblk <= kb keep all their
+ * blocks in `blocks`, but select their k2 best from the keys.
+ * Why (the prefill PR, "The interface": the source layer takes its own
+ * top-512): with k2 = k + 1 the source's dense top-k lies inside these k2
+ * blocks -- every block holding one of the k best positions has at most k - 1
+ * blocks other than the newest above it, with ties going to lower ids at both
+ * levels -- so scoring just these 8 k2 positions per row gives the top-k
+ * exactly, without the dense score matrix.
+ */
+idx_status idx_topk_blocks_nested(const float* keys, int64_t ldk, const int32_t* len, int32_t rows,
+                                  int32_t kb, int32_t* blocks, int32_t* n_kept, int32_t k2,
+                                  int32_t* blocks2, int32_t* n_kept2, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /*
  * idx_expand_candidates -- pool blocks, valid lengths and the sparse work list

@@ -331,6 +331,36 @@ def test_topk_blocks_bitexact(idx, kb, maxblk):
     assert np.array_equal(host(blocks), bo)
 
 
+@pytest.mark.parametrize("kb,k2,maxblk", [(2048, 513, 32768), (2048, 513, 8192), (16, 5, 128),
+                                          (64, 64, 8192), (2048, 1, 4000), (3, 2, 40), (1024, 33, 1500)])
+def test_topk_blocks_nested_bitexact(idx, kb, k2, maxblk):
+    """idx_topk_blocks_nested: the kb best blocks exactly as idx_topk_blocks, and
+    the k2 best by the same rule, including rows that keep all kb but have more
+    than k2 blocks (selected from their keys) and rows with at most k2 blocks."""
+    rows = 48
+    keys = workloads.random_matrix(kb + maxblk + k2, rows, maxblk)
+    extra = [0, 1, k2 - 1, k2, k2 + 1, kb - 1, kb, kb + 1, 2 * kb, maxblk, maxblk - 1]
+    nb = workloads.random_lengths(kb + maxblk + 1, rows, 0, maxblk,
+                                  extra=[e for e in extra if 0 <= e <= maxblk])
+    lens = (nb * 8 - (np.arange(rows) % 8)).clip(0).astype(np.int32)
+    nblk = oracle.nblocks(lens)
+    for r in range(rows):
+        if nblk[r] > 0:
+            keys[r, nblk[r] - 1] = np.inf
+    say(f"topk_blocks_nested kb={kb} k2={k2} maxblk={maxblk}")
+    blocks = torch.full((rows, kb), -5, dtype=torch.int32, device="cuda")
+    n_kept = torch.full((rows,), -5, dtype=torch.int32, device="cuda")
+    blocks2 = torch.full((rows, k2), -5, dtype=torch.int32, device="cuda")
+    n_kept2 = torch.full((rows,), -5, dtype=torch.int32, device="cuda")
+    idx.idx_topk_blocks_nested(dev(keys), dev(lens), kb, blocks, n_kept, k2, blocks2, n_kept2)
+    bo, no = oracle.select_blocks(keys, lens, kb)
+    b2, n2 = oracle.select_blocks(keys, lens, k2)
+    assert np.array_equal(host(n_kept), no)
+    assert np.array_equal(host(blocks), bo)
+    assert np.array_equal(host(n_kept2), n2)
+    assert np.array_equal(host(blocks2), b2)
+
+
 # ---------------------------------------------------------------------------
 # idx_topk_rows (bit-exact, three column modes)
 # ---------------------------------------------------------------------------
@@ -469,6 +499,17 @@ def test_topk_mapped_and_blocks_crowded(idx, kind, cluster):
     bo, no = oracle.select_blocks(keys, lens, kb)
     assert np.array_equal(host(n_kept), no)
     assert np.array_equal(host(bl), bo)
+    say(f"topk_blocks_nested crowded {kind}/{cluster}")
+    k2 = 513
+    bl2 = torch.full((rows, k2), -5, dtype=torch.int32, device="cuda")
+    nk2 = torch.full((rows,), -5, dtype=torch.int32, device="cuda")
+    bl.fill_(-5)
+    n_kept.fill_(-5)
+    idx.idx_topk_blocks_nested(dev(keys), dev(lens), kb, bl, n_kept, k2, bl2, nk2)
+    b2, n2 = oracle.select_blocks(keys, lens, k2)
+    assert np.array_equal(host(bl), bo) and np.array_equal(host(n_kept), no)
+    assert np.array_equal(host(nk2), n2)
+    assert np.array_equal(host(bl2), b2)
 
 
 # ---------------------------------------------------------------------------
@@ -668,9 +709,30 @@ def _check_chunk(wl, ch, rows, n_consumers):
     selection up to ties within tolerance of the k-th score; and the consumer
     scores still held in the chunk's score buffers element by element."""
     res = oracle.run_chunk(wl, row_ids=rows, n_consumers=n_consumers)
-    Sg = host(ch.S)[rows]
-    valid = np.arange(wl.ld)[None, :] < wl.lens[rows][:, None]
-    assert_close(Sg, res["S"], valid, f"{wl.name} chunk dense")
+    if ch.S is not None:   # (a chunk that rescores the source's candidates has no S)
+        Sg = host(ch.S)[rows]
+        valid = np.arange(wl.ld)[None, :] < wl.lens[rows][:, None]
+        assert_close(Sg, res["S"], valid, f"{wl.name} chunk dense")
+    if ch.rescore:
+        # the source's top-(k+1) blocks (nested in its kb best) and their scores
+        b2 = host(ch.table2.blocks)[rows]
+        nk2 = host(ch.table2.n_kept)[rows]
+        T2 = host(ch.T_src)[rows]
+        v2 = host(ch.table2.valid_len)[rows]
+        keys2 = oracle.block_keys(res["S"], wl.lens[rows], ch.k2, ldk=wl.ldk)   # keyed past k + 1
+        for i, r in enumerate(rows):
+            nb = int(oracle.nblocks(wl.lens[r:r + 1])[0])
+            assert nk2[i] == min(nb, ch.k2), f"row {r}: {nk2[i]} nested blocks"
+            kept = set(int(x) for x in b2[i, :nk2[i]])
+            if nb > ch.k2:
+                kth = kth_largest(keys2[i, :nb], ch.k2)
+                order = np.lexsort((np.arange(nb), -keys2[i, :nb].astype(np.float64)))
+                want = set(int(x) for x in order[:ch.k2])
+                for x in kept ^ want:
+                    assert within_tol(keys2[i, x], kth), f"row {r}: nested block {x}"
+            pos = oracle.candidate_positions(b2[i:i + 1], v2[i:i + 1])[0, :v2[i]]
+            assert_close(T2[i:i + 1, :v2[i]], res["S"][i:i + 1, pos], np.ones((1, v2[i]), bool),
+                         f"{wl.name} row {r} rescored source scores")
     blocks_g = host(ch.table.blocks)[rows]
     n_kept_g = host(ch.table.n_kept)[rows]
     valid_g = host(ch.table.valid_len)[rows]
@@ -773,18 +835,57 @@ def test_chunk_bf16_consumers(idx, name):
     _check_bf16_agreement(wl, ch, rows, nc)
 
 
-def test_chunk_tiny(idx):
+@pytest.mark.parametrize("source", ["rescore", "dense"])
+def test_chunk_tiny(idx, source):
+    from two_level_top_amd.chunk import Chunk
     wl = workloads.tiny()
-    say("chunk tiny")
-    ch = _run_chunk(idx, wl)
+    say(f"chunk tiny, source top-k from {source}")
+    ch = Chunk(wl, source_scores=source)
+    ch.run()
+    torch.cuda.synchronize()
     _check_chunk(wl, ch, np.arange(wl.rows), None)
 
 
-def test_chunk_decode(idx):
+@pytest.mark.parametrize("source", ["rescore", "dense"])
+def test_chunk_decode(idx, source):
+    from two_level_top_amd.chunk import Chunk
     wl = workloads.decode(n_consumers=2)
-    say("chunk decode (64 requests x 1 row)")
-    ch = _run_chunk(idx, wl)
+    say(f"chunk decode (64 requests x 1 row), source top-k from {source}")
+    ch = Chunk(wl, source_scores=source)
+    ch.run()
+    torch.cuda.synchronize()
     _check_chunk(wl, ch, np.arange(0, 64, 4), None)
+
+
+def test_chunk_long_dense_source(idx):
+    """The long chunk with the source's top-k taken from the dense score matrix
+    (GATHER over the candidate columns): sampled rows against the oracle."""
+    from two_level_top_amd.chunk import Chunk
+    wl = workloads.long_chunk(n_consumers=1)
+    say("chunk long, source top-k from the dense score matrix")
+    ch = Chunk(wl, source_scores="dense")
+    ch.run()
+    torch.cuda.synchronize()
+    _check_chunk(wl, ch, np.array([0, 7, 9000, 16383]), 1)
+
+
+def test_keys_only_pass_matches_keys_with_scores(idx):
+    """idx_score_dense_keys without S writes the same keys as with S."""
+    from two_level_top_amd.chunk import Chunk
+    for wl in (workloads.tiny(), workloads.decode(n_consumers=0)):
+        say(f"keys-only dense pass, {wl.name}")
+        ch = Chunk(wl, n_consumers=0, source_scores="dense")
+        L = wl.layers[0]
+        q = idx.Query(dev(L.qv), dev(L.qs), dev(L.w))
+        k1 = torch.full((wl.rows, wl.ldk), -7.0, dtype=torch.float32, device="cuda")
+        k2 = torch.full_like(k1, -7.0)
+        S = torch.empty((wl.rows, wl.ld), dtype=torch.float32, device="cuda")
+        for skip in (0, 9):
+            k1.fill_(-7.0)
+            k2.fill_(-7.0)
+            idx.idx_score_dense_keys(q, ch.kp, ch.rows, S, k1, skip_le_blocks=skip)
+            idx.idx_score_dense_keys(q, ch.kp, ch.rows, None, k2, skip_le_blocks=skip, ld=wl.ld)
+            assert bool((k1 == k2).all()), f"{wl.name} skip={skip}"
 
 
 def test_chunk_decode_overlap_matches_serial(idx):
@@ -821,11 +922,14 @@ def test_chunk_graph_replay(idx):
     ch.run()
     torch.cuda.synchronize()
     names = ("blocks", "n_kept", "phys", "valid_len")
-    ref = {"S": host(ch.S), "src": host(ch.src_top), **{n: host(getattr(ch.table, n)) for n in names}}
+    ref = {"src": host(ch.src_top), **{n: host(getattr(ch.table, n)) for n in names}}
+    if ch.S is not None:
+        ref["S"] = host(ch.S)
     ref_c = [host(t) for t in ch.cons_top]
     ch.capture()
     for _ in range(3):
-        ch.S.fill_(float("nan"))
+        if ch.S is not None:
+            ch.S.fill_(float("nan"))
         ch.src_top.fill_(-7)
         for t in ch.cons_top:
             t.fill_(-7)
@@ -835,7 +939,8 @@ def test_chunk_graph_replay(idx):
         ch.replay()
         torch.cuda.synchronize()
         valid = np.arange(wl.ld)[None, :] < wl.lens[:, None]   # S past len is never written
-        assert np.array_equal(host(ch.S)[valid], ref["S"][valid])
+        if ch.S is not None:
+            assert np.array_equal(host(ch.S)[valid], ref["S"][valid])
         assert np.array_equal(host(ch.src_top), ref["src"])
         for t, r in zip(ch.cons_top, ref_c):
             assert np.array_equal(host(t), r)

@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "IdxError", "Query", "KPool", "Rows", "Table", "load",
-    "idx_score_dense", "idx_score_dense_keys", "idx_q_rope_quant", "idx_amax8_varlen", "idx_topk_blocks", "idx_expand_candidates",
+    "idx_score_dense", "idx_score_dense_keys", "idx_q_rope_quant", "idx_amax8_varlen", "idx_topk_blocks",
+    "idx_topk_blocks_nested", "idx_expand_candidates",
     "idx_score_sparse_paged", "idx_score_sparse_paged_bf16", "idx_score_sparse_paged_noalloc",
     "idx_topk_rows", "idx_topk_rows_bf16",
     "idx_prefill_tail", "idx_workspace_bytes",
@@ -86,6 +87,7 @@ def load():
         "idx_q_rope_quant": [_P, _P, _P, _I32, _P, _I32, _I32, _I32, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P],
         "idx_score_dense_keys": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), _P, _I64, _P, _I64, _I32, _P, ctypes.c_size_t, _P],
         "idx_topk_blocks": [_P, _I64, _P, _I32, _I32, _P, _P, _P, ctypes.c_size_t, _P],
+        "idx_topk_blocks_nested": [_P, _I64, _P, _I32, _I32, _P, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
         "idx_expand_candidates": [ctypes.POINTER(_KPool), ctypes.POINTER(_Rows), ctypes.POINTER(_Table), _P],
         "idx_score_sparse_paged": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_topk_rows": [_P, _I64, _P, _I32, _I32, ctypes.c_int, _P, _I32, _P, _P, _P, ctypes.c_size_t, _P],
@@ -312,17 +314,23 @@ def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, ws=None, s
            "idx_score_dense")
 
 
-def idx_score_dense_keys(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, keys: torch.Tensor,
-                         skip_le_blocks: int = 0, ws=None, stream=None):
+def idx_score_dense_keys(q: Query, kp: KPool, rows: Rows, S: torch.Tensor | None, keys: torch.Tensor,
+                         skip_le_blocks: int = 0, ws=None, stream=None, ld: int | None = None):
+    """S=None: keys only (the scores are never written); then `ld` (>= the longest
+    row, a multiple of 8) must be given, as the stride the scores would have."""
     if q.rows != rows.rows:
         raise IdxError(f"query rows {q.rows} != rows {rows.rows}")
-    _req(S, torch.float32, "S", rows=rows.rows, gpu=False)
+    if S is not None:
+        _req(S, torch.float32, "S", rows=rows.rows, gpu=False)
+        ld = S.stride(0)
+    elif ld is None:
+        raise IdxError("keys only (S=None) needs ld")
     _req(keys, torch.float32, "keys", rows=rows.rows, gpu=False)
     _on_gpu(S, keys, names=("S", "keys"))
-    ws = _score_ws(ws, q.rows, S.device, stream)
+    ws = _score_ws(ws, q.rows, keys.device, stream)
     q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
     _check(load().idx_score_dense_keys(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
-                                       _ptr(S), S.stride(0), _ptr(keys), keys.stride(0),
+                                       _ptr(S), int(ld), _ptr(keys), keys.stride(0),
                                        int(skip_le_blocks), _ptr(ws), ws.numel(), _stream(stream)),
            "idx_score_dense_keys")
 
@@ -380,6 +388,24 @@ def idx_topk_blocks(keys, lens, kb: int, blocks, n_kept, stream=None):
            "idx_topk_blocks")
 
 
+def idx_topk_blocks_nested(keys, lens, kb: int, blocks, n_kept, k2: int, blocks2, n_kept2,
+                           stream=None):
+    _req(lens, torch.int32, "len", gpu=False)
+    n = int(lens.shape[0]) if lens.dim() == 1 else -1
+    _req(keys, torch.float32, "keys", rows=n, gpu=False)
+    for name, t in (("blocks", blocks), ("n_kept", n_kept), ("blocks2", blocks2), ("n_kept2", n_kept2)):
+        _req(t, torch.int32, name, rows=n, gpu=False)
+    if blocks.dim() != 2 or blocks.shape[-1] != kb:
+        raise IdxError("blocks must be [rows, kb]")
+    if blocks2.dim() != 2 or blocks2.shape[-1] != k2:
+        raise IdxError("blocks2 must be [rows, k2]")
+    _on_gpu(keys, lens, blocks, n_kept, blocks2, n_kept2,
+            names=("keys", "len", "blocks", "n_kept", "blocks2", "n_kept2"))
+    _check(load().idx_topk_blocks_nested(_ptr(keys), keys.stride(0), _ptr(lens), n, kb, _ptr(blocks),
+                                         _ptr(n_kept), k2, _ptr(blocks2), _ptr(n_kept2), None, 0,
+                                         _stream(stream)), "idx_topk_blocks_nested")
+
+
 def idx_expand_candidates(kp: KPool, rows: Rows, tbl: Table, stream=None):
     if tbl.rows != rows.rows:
         raise IdxError(f"table rows {tbl.rows} != rows {rows.rows}")
@@ -396,10 +422,15 @@ def _sparse_args(q: Query, tbl: Table, T: torch.Tensor, dtype):
     _on_gpu(T, names=("T",))
 
 
-def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=None, stream=None):
+def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=None, stream=None,
+                           wait_ready: bool = True):
+    """wait_ready=False: the call runs on the stream that built the table, so it does
+    not wait on the table's ready event (a stream never waits on an event it recorded)."""
     _sparse_args(q, tbl, T, torch.float32)
     ws = _score_ws(ws, q.rows, T.device, stream)
     q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
+    if not wait_ready:
+        t_c.ready = None
     _check(load().idx_score_sparse_paged(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
                                          _ptr(T), T.stride(0), _ptr(ws), ws.numel(),
                                          _stream(stream)),

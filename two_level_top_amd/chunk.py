@@ -59,8 +59,8 @@ import torch
 from . import (COLS_BLOCKMAP, COLS_GATHER, COLS_IDENTITY, KPool, Query, Rows, Table,
                idx_amax8_varlen, idx_expand_candidates, idx_prefill_tail, idx_score_dense,
                idx_score_dense_keys, idx_score_sparse_paged, idx_score_sparse_paged_bf16,
-               idx_topk_blocks, idx_topk_rows, idx_topk_rows_bf16, score_workspace,
-               stream_wait_table, tail_workspace)
+               idx_topk_blocks, idx_topk_blocks_nested, idx_topk_rows, idx_topk_rows_bf16,
+               score_workspace, stream_wait_table, tail_workspace)
 
 
 def _dev(a, dtype, device):
@@ -96,7 +96,7 @@ class Chunk:
 
     def __init__(self, wl, device="cuda", n_consumers=None, k_source=None, with_offset=True,
                  share_T=True, fused_keys=True, consumer_bf16=False, overlap_selects=None,
-                 source_side=True, tail_layers=0):
+                 source_side=True, tail_layers=0, source_scores="rescore"):
         self.wl = wl
         self.fused_keys = fused_keys
         self.consumer_bf16 = consumer_bf16   # consumers write and select bf16 scores
@@ -110,9 +110,20 @@ class Chunk:
         layers = wl.layers if n_consumers is None else wl.layers[:1 + n_consumers]
         self.queries = [Query(_dev(L.qv, torch.uint8, device), _dev(L.qs, torch.uint8, device),
                               _dev(L.w, torch.float32, device)) for L in layers]
-        self.S = torch.empty((self.R, self.ld), dtype=torch.float32, device=device)
+        # source top-k: "rescore" its top-(k+1) blocks (keys-only dense pass, no
+        # score matrix), or take it from the "dense" score matrix S
+        if source_scores not in ("rescore", "dense"):
+            raise ValueError("source_scores must be 'rescore' or 'dense'")
+        self.k2 = self.k_src + 1
+        self.rescore = source_scores == "rescore" and fused_keys and self.k2 <= self.kb
+        self.S = None if self.rescore else \
+            torch.empty((self.R, self.ld), dtype=torch.float32, device=device)
         self.keys = torch.empty((self.R, self.ldk), dtype=torch.float32, device=device)
         self.table = Table(self.R, self.kb, device)
+        if self.rescore:
+            self.table2 = Table(self.R, self.k2, device)   # the source's top-(k+1) blocks
+            self.T_src = torch.empty((self.R, self.k2 * 8), dtype=torch.float32, device=device)
+            self.ws_src = score_workspace(self.R, device)  # the source fold, on the side stream
         ncons = len(self.queries) - 1
         self.overlap = (self.R <= self.OVERLAP_MAX_ROWS) if overlap_selects is None else overlap_selects
         nT = max(1, ncons) if not share_T else (min(2, max(1, ncons)) if self.overlap else 1)
@@ -161,7 +172,10 @@ class Chunk:
     # -- the source layer ---------------------------------------------------
     def score_source(self, stream=None):
         self._mark("dense<")
-        if self.fused_keys:
+        if self.rescore:   # keys only; rows with more than k + 1 blocks are keyed
+            idx_score_dense_keys(self.queries[0], self.kp, self.rows, None, self.keys,
+                                 skip_le_blocks=self.k2, ws=self.ws, stream=stream, ld=self.ld)
+        elif self.fused_keys:
             idx_score_dense_keys(self.queries[0], self.kp, self.rows, self.S, self.keys,
                                  skip_le_blocks=self.kb, ws=self.ws, stream=stream)
         else:
@@ -174,9 +188,13 @@ class Chunk:
         self.scores_ready.record(main)
         self.side.wait_event(self.scores_ready)
         if not torch.cuda.is_current_stream_capturing():   # (a graph keeps its buffers alive)
-            for t in (self.S, self.keys, *self.table.tensors(), self.rows.req, self.rows.len,
-                      self.src_top, *((self.rows.pos_offset,) if self.rows.pos_offset is not None else ())):
+            for t in (self.keys, *self.table.tensors(), self.rows.req, self.rows.len, self.src_top,
+                      *((self.S,) if self.S is not None else ()),
+                      *((self.rows.pos_offset,) if self.rows.pos_offset is not None else ())):
                 t.record_stream(self.side)
+            if self.rescore:
+                for t in (*self.table2.tensors(), self.T_src, self.ws_src):
+                    t.record_stream(self.side)
             if self.tail is not None:
                 for t in (*self.tail.tensors(), self.tail_rpr, self.tail_len, self.tail_ws):
                     t.record_stream(self.side)
@@ -186,7 +204,11 @@ class Chunk:
                 idx_amax8_varlen(self.S, self.rows.len, self.keys, skip_le_blocks=self.kb)
                 self._mark("amax8>")
             self._mark("topk_blocks<")
-            idx_topk_blocks(self.keys, self.rows.len, self.kb, self.table.blocks, self.table.n_kept)
+            if self.rescore:
+                idx_topk_blocks_nested(self.keys, self.rows.len, self.kb, self.table.blocks,
+                                       self.table.n_kept, self.k2, self.table2.blocks, self.table2.n_kept)
+            else:
+                idx_topk_blocks(self.keys, self.rows.len, self.kb, self.table.blocks, self.table.n_kept)
             self._mark("topk_blocks>")
             idx_expand_candidates(self.kp, self.rows, self.table)   # records table.ready
             self._mark("expand>")
@@ -194,8 +216,22 @@ class Chunk:
                 idx_prefill_tail(self.table, self.tail_rpr, self.tail_len, self.tail, ws=self.tail_ws,
                                  wait_full=False)
                 self._mark("tail>")
+            if self.rescore:
+                # the source's own top-k: its scores at its top-(k+1) blocks (the
+                # consumers start on table.ready meanwhile)
+                idx_expand_candidates(self.kp, self.rows, self.table2)
+                self._mark("source_topk<")
+                idx_score_sparse_paged(self.queries[0], self.kp, self.table2, self.T_src, ws=self.ws_src,
+                                       wait_ready=False)
+                idx_topk_rows(self.T_src, self.table2.valid_len, self.k_src, self.src_top,
+                              mode=COLS_BLOCKMAP, blocks=self.table2.blocks,
+                              pos_offset=self.rows.pos_offset)
+                self._mark("source_topk>")
+                self.source_done.record(self.side)
 
     def source_topk(self, same_stream_as_table=False):
+        if self.rescore:
+            return   # taken in publish(), on the side stream
         """The source's own top-k (waits for the table when it reads it, unless it
         runs on the stream that built the table: a stream never waits on an event
         it recorded itself, which a graph capture cannot express)."""
@@ -254,6 +290,10 @@ class Chunk:
                 main.wait_stream(self.sel)
 
     def _run_layers(self, main):
+        if self.rescore:   # the source's top-k runs inside publish(), on the side stream
+            self._run_consumers(main)
+            main.wait_event(self.source_done)
+            return
         if not self.overlap:
             if self.source_side:
                 # the source's own top-k (HBM-bound: it gathers S at the
@@ -273,6 +313,13 @@ class Chunk:
         with _forked(self.sel, main):
             self.sel.wait_event(self.scores_ready)
             self.source_topk()
+        self._run_consumers(main)
+
+    def _run_consumers(self, main):
+        if not self.overlap:
+            for i in range(len(self.cons_top)):
+                self.consumer(i)
+            return
         nT = len(self.T)
         for i in range(len(self.cons_top)):
             T = self.T[i % nT]

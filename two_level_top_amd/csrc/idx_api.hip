@@ -185,7 +185,7 @@ static idx_status score_dense_impl(const idx_query* q, const idx_kpool* kp, cons
     if (ldk < 1) return fail(IDX_E_ARG, "%s: ldk must hold at least one key per row", fn);
   }
   if (rows->rows == 0) return ok();
-  if (!S) return fail(IDX_E_ARG, "%s: S is NULL", fn);
+  if (!S && !keys) return fail(IDX_E_ARG, "%s: S is NULL", fn);   // (keys only: S may be NULL)
   if (!aligned(S, 4)) return fail(IDX_E_ALIGN, "%s: S must be 4-byte aligned", fn);
   if (keys && !aligned(keys, 4)) return fail(IDX_E_ALIGN, "%s: keys must be 4-byte aligned", fn);
   TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
@@ -262,7 +262,26 @@ idx_status idx_topk_blocks(const float* keys, int64_t ldk, const int32_t* len, i
   if (rows == 0) return ok();
   if (!keys || !len || !blocks || !n_kept) return fail(IDX_E_ARG, "%s: a pointer is NULL", fn);
   return hip_status(idxk::launch_topk(3, keys, false, ldk, nullptr, len, rows, kb, ldk, nullptr, kb,
-                                      nullptr, blocks, n_kept, stream), fn);
+                                      nullptr, blocks, n_kept, 0, nullptr, nullptr, stream), fn);
+}
+
+idx_status idx_topk_blocks_nested(const float* keys, int64_t ldk, const int32_t* len, int32_t rows,
+                                  int32_t kb, int32_t* blocks, int32_t* n_kept, int32_t k2,
+                                  int32_t* blocks2, int32_t* n_kept2, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  const char* fn = "idx_topk_blocks_nested";
+  (void)ws;
+  (void)ws_bytes;
+  if (rows < 0) return fail(IDX_E_ARG, "%s: rows < 0", fn);
+  if (kb < 1) return fail(IDX_E_ARG, "%s: kb < 1", fn);
+  if (k2 < 1 || k2 > kb) return fail(IDX_E_ARG, "%s: k2 %d outside [1, kb = %d]", fn, k2, kb);
+  if (kb > 4096) return fail(IDX_E_UNSUPPORTED, "%s: kb %d above 4096", fn, kb);
+  if (ldk < 1) return fail(IDX_E_ARG, "%s: ldk < 1", fn);
+  if (rows == 0) return ok();
+  if (!keys || !len || !blocks || !n_kept || !blocks2 || !n_kept2)
+    return fail(IDX_E_ARG, "%s: a pointer is NULL", fn);
+  return hip_status(idxk::launch_topk(3, keys, false, ldk, nullptr, len, rows, kb, ldk, nullptr, kb,
+                                      nullptr, blocks, n_kept, k2, blocks2, n_kept2, stream), fn);
 }
 
 idx_status idx_expand_candidates(const idx_kpool* kp, const idx_rows* rows, idx_table* tbl,
@@ -360,7 +379,7 @@ static idx_status topk_rows_impl(const void* X, bool bf16, int64_t ld, const int
   // widest row the call can see: ld columns, or kb * 8 candidate columns
   const int64_t width = mode == IDX_COLS_IDENTITY ? ld : (int64_t)kb * idxk::kBlock;
   return hip_status(idxk::launch_topk(mode, X, bf16, ld, valid, nullptr, rows, k, width, blocks, kb,
-                                      pos_offset, out, nullptr, stream), fn);
+                                      pos_offset, out, nullptr, 0, nullptr, nullptr, stream), fn);
 }
 
 idx_status idx_topk_rows(const float* X, int64_t ld, const int32_t* valid, int32_t rows, int32_t k,

@@ -56,10 +56,11 @@ hipError_t launch_amax8(const float* S, int64_t ld, const int32_t* len, int rows
 
 // mode: 0 identity, 1 blockmap, 2 gather, 3 block keys (idx_topk_blocks)
 // bf16: X holds bf16 values (modes 0-2)
+// mode 3 with k2 > 0: also the k2 best (k2 <= k) into out2 / n_kept2
 hipError_t launch_topk(int mode, const void* X, bool bf16, int64_t ld, const int32_t* nvalid,
                        const int32_t* len_for_blocks, int rows, int k, int64_t max_cols,
                        const int32_t* blocks, int kb, const int32_t* pos_offset, int32_t* out,
-                       int32_t* n_kept, hipStream_t st);
+                       int32_t* n_kept, int k2, int32_t* out2, int32_t* n_kept2, hipStream_t st);
 
 hipError_t launch_expand(const PoolArgs& kp, const int32_t* req, const int32_t* len, int rows,
                          int kb, const int32_t* blocks, const int32_t* n_kept, int32_t* phys,

@@ -51,6 +51,11 @@ constexpr int kDenseRowsPerWave = 2;
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// What a launch writes: the scores, the block keys, or both (a keys-only pass
+// never materialises the score matrix).
+constexpr int kOutScores = 1;
+constexpr int kOutKeys = 2;
+
 // Where the fused block keys go (keys == nullptr: not requested).
 struct KeyArgs {
   float* keys;
@@ -96,10 +101,10 @@ __device__ __forceinline__ int page_tile_scale(const PageOps& o, int t, int sdis
 
 // Score NR (1 or 2) rows of one request against positions [c0, cend) (c0 on
 // a page boundary, at most 16 pages).  Every tile of a page is computed;
-// positions past a row's length are never stored.  With KEYS, Krow[r] gets
+// positions past a row's length are never stored.  With keys, Krow[r] gets
 // the keys of blocks [c0/8, min(cend/8, nblk[r])) (Krow[r] is only used when
 // nblk[r] > 0, i.e. the row is keyed).
-template <int HB, int NR, bool KEYS>
+template <int HB, int NR, int OUTS>
 __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const PairFold& pf,
                                            float* const (&Srow)[2],
                                            const int (&lens)[2], float* const (&Krow)[2],
@@ -149,8 +154,9 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const Pair
     for (int r = 0; r < NR; ++r) {
       const float tot = reduce_scatter4(part[r][0], part[r][1], part[r][2], part[r][3]);
       const uint32_t rem = lens[r] > pb0 ? (uint32_t)(lens[r] - pb0) * 4u : 0u;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), buffer_rsrc(Srow[r] + pb0, rem), soffs, 0, 0);
-      if (KEYS) {
+      if (OUTS & kOutScores)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tot), buffer_rsrc(Srow[r] + pb0, rem), soffs, 0, 0);
+      if (OUTS & kOutKeys) {
         float key = max8_lanes(tot);
         const int newest = nblk[r] - 1 - kb0;   // the newest block's index in the page
         if (newest >= 0 && newest < kBlocksPerPage)   // (uniform) its key is +inf
@@ -171,7 +177,7 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const Pair
   }
 }
 
-template <int HB, bool KEYS>
+template <int HB, int OUTS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_dense_kernel(QueryArgs q, const uint8_t* __restrict__ fold,
                                                           PoolArgs kp,
                                                           const int32_t* __restrict__ req,
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   // nblk = 0 marks a row without keys
   int nblk[2] = {0, 0};
   float* Krow[2] = {nullptr, nullptr};
-  if (KEYS) {
+  if (OUTS & kOutKeys) {
     const int64_t kcap = min(ka.ldk, ld / kBlock);
     const int nb0 = (int)min((int64_t)((len0 + kBlock - 1) / kBlock), kcap);
     const int nb1 = (int)min((int64_t)((len1 + kBlock - 1) / kBlock), kcap);
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     Srow[1] = S + (int64_t)r1 * ld;
     lens[0] = len0;
     lens[1] = len1;
-    score_rows<HB, 2, KEYS>(f, pf, Srow, lens, Krow, nblk, kp.pool, kp.num_pages,
+    score_rows<HB, 2, OUTS>(f, pf, Srow, lens, Krow, nblk, kp.pool, kp.num_pages,
                             kp.page_table + (int64_t)req0 * kp.max_pages, kp.max_pages, c0, cend, lane);
     return;
   }
@@ -240,20 +246,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
     lens[1] = 0;
     float* const Kr[2] = {Krow[i], Krow[i]};
     const int nb[2] = {nblk[i], 0};
-    score_rows<HB, 1, KEYS>(f, pf, Srow, lens, Kr, nb, kp.pool, kp.num_pages,
+    score_rows<HB, 1, OUTS>(f, pf, Srow, lens, Kr, nb, kp.pool, kp.num_pages,
                             kp.page_table + (int64_t)rq * kp.max_pages, kp.max_pages, c0, cend, lane);
   }
 }
 
-template <bool KEYS>
+template <int OUTS>
 static void launch_dense_hb(int hb, dim3 grid, hipStream_t st, const QueryArgs& q, const uint8_t* fold,
                             const PoolArgs& kp, const int32_t* req, const int32_t* len, float* S,
                             int64_t ld, const KeyArgs& ka, int nchunks, int chunk_len) {
   switch (hb) {
-    case 1: hipLaunchKernelGGL((score_dense_kernel<1, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
-    case 2: hipLaunchKernelGGL((score_dense_kernel<2, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
-    case 3: hipLaunchKernelGGL((score_dense_kernel<3, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
-    default: hipLaunchKernelGGL((score_dense_kernel<4, KEYS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
+    case 1: hipLaunchKernelGGL((score_dense_kernel<1, OUTS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
+    case 2: hipLaunchKernelGGL((score_dense_kernel<2, OUTS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
+    case 3: hipLaunchKernelGGL((score_dense_kernel<3, OUTS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
+    default: hipLaunchKernelGGL((score_dense_kernel<4, OUTS>), grid, dim3(256), 0, st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len); break;
   }
 }
 
@@ -271,10 +277,12 @@ hipError_t launch_score_dense(const QueryArgs& q, const uint8_t* fold, const Poo
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int hb = (q.heads + 15) / 16;
   const KeyArgs ka{keys, ldk, skip};
-  if (keys)
-    launch_dense_hb<true>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len);
+  if (keys && S)
+    launch_dense_hb<kOutScores | kOutKeys>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len);
+  else if (keys)
+    launch_dense_hb<kOutKeys>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len);
   else
-    launch_dense_hb<false>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len);
+    launch_dense_hb<kOutScores>(hb, dim3((unsigned)grid), st, q, fold, kp, req, len, S, ld, ka, nchunks, chunk_len);
   return hipGetLastError();
 }
 

@@ -78,6 +78,9 @@ struct TopkArgs {
   const int32_t* pos_offset;
   int32_t* out;            // [rows][k]
   int32_t* n_kept;         // mode 3
+  int k2;                  // mode 3, > 0: also the k2 best blocks (k2 <= k) ...
+  int32_t* out2;           // ... into out2 [rows][k2]
+  int32_t* n_kept2;        // ... and n_kept2 [rows]
 };
 
 constexpr uint32_t kCand = 4096;   // register path: keys of the threshold bin
@@ -247,7 +250,9 @@ __device__ __forceinline__ int find_bin(Sh& sh, uint32_t rem, uint32_t* above_ou
 }
 
 // RESIDENT: every row fits one chunk (n <= THREADS * 32), loaded once.
-template <int MODE, bool VEC, int THREADS, bool RESIDENT, bool BF16>
+// NEST (block keys only): also the nested k2 best blocks (a kernel of its own,
+// so that the plain block selection carries none of it)
+template <int MODE, bool VEC, int THREADS, bool RESIDENT, bool BF16, bool NEST = false>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDENT ? 4 : THREADS == 1024 ? 8 : THREADS == 512 ? 6 : 4))) void topk_kernel(TopkArgs a) {
   constexpr int W = THREADS / 64;
   constexpr int kChunk = W * kWaveSlice;
@@ -269,19 +274,36 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
     if (kMapped && n > a.kb * kBlock) n = a.kb * kBlock;
   }
   if (MODE != MODE_GATHER && (int64_t)n > a.ld) n = (int)a.ld;   // never read past the row
-  const int k = a.k;
-  int32_t* out = a.out + (int64_t)row * k;
   const int32_t pad = MODE == MODE_KEYS ? 0x7fffffff : -1;
   const int32_t off = (MODE != MODE_KEYS && a.pos_offset) ? a.pos_offset[row] : 0;
   const int32_t* blk = kMapped ? a.blocks + (int64_t)row * a.kb : nullptr;
   const void* Xr = BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(a.X) + (int64_t)row * a.ld)
                         : static_cast<const void*>(static_cast<const float*>(a.X) + (int64_t)row * a.ld);
+  // block keys: the kb best into out and, nested in them, the k2 best into
+  // out2 (the source's own top-(k+1) blocks).  The list from which the kb
+  // best are written (or, on the register path, the list of the kb best
+  // themselves) holds the k2 best too, so the second selection runs on it.
+  // A row that keeps all its blocks selects only its k2 best ("second").
+  const bool want2 = NEST && MODE == MODE_KEYS && a.k2 > 0;
+  bool second = false;
 
-  if (n <= k) {  // every column is kept
-    for (int i = tid; i < k; i += THREADS) out[i] = i < n ? map_index<MODE>(blk, i) + off : pad;
+  if (n <= a.k) {  // every column is kept
+    int32_t* out = a.out + (int64_t)row * a.k;
+    for (int i = tid; i < a.k; i += THREADS) out[i] = i < n ? map_index<MODE>(blk, i) + off : pad;
     if (MODE == MODE_KEYS && tid == 0) a.n_kept[row] = n;
-    return;
+    if (!want2) return;
+    if (n <= a.k2) {
+      int32_t* out2 = a.out2 + (int64_t)row * a.k2;
+      for (int i = tid; i < a.k2; i += THREADS) out2[i] = i < n ? i : pad;
+      if (tid == 0) a.n_kept2[row] = n;
+      return;
+    }
+    second = true;
   }
+  const bool nest = want2 && !second;   // a second selection on the list
+  const int k = second ? a.k2 : a.k;
+  int32_t* const out = second ? a.out2 + (int64_t)row * a.k2 : a.out + (int64_t)row * a.k;
+  int32_t* const n_kept = second ? a.n_kept2 : a.n_kept;
 
   const int nchunks = RESIDENT ? 1 : (n + kChunk - 1) / kChunk;
   uint32_t key[kTopkSteps][4];
@@ -361,8 +383,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
 
   // on the m list entries: fix the bits of K - base below `low` (the bits
   // above are `fixed`; `need` counts the entries still to take from those
-  // with the fixed high bits), then write the kept entries in list order
-  auto refine_output = [&](uint32_t base, uint32_t fixed, int low, uint32_t need, uint32_t m) {
+  // with the fixed high bits), then write the kept entries in list order to
+  // out; kk = the row's selection size (recorded in n_kept for block keys)
+  auto refine_output = [&](uint32_t base, uint32_t fixed, int low, uint32_t need, uint32_t m,
+                           int32_t* out, int32_t* n_kept, int kk) {
     // ---- 3a. refine the low bits of K on the list ----
     while (low > 0) {
       const int width = low < 11 ? low : 11;
@@ -408,8 +432,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       gpre += g ? 1u : 0u;
       qpre += q ? 1u : 0u;
     }
-    if (MODE == MODE_KEYS && tid == 0) a.n_kept[row] = k;
+    if (MODE == MODE_KEYS && tid == 0) n_kept[row] = kk;
   };
+
+  // the k2 best blocks from the list of a first selection: every entry is at
+  // or above `bound`, and the list holds at least k2 entries
+  auto nested_output = [&](uint32_t bound, uint32_t m) {
+    __syncthreads();   // the first output has read the list counts
+    const uint32_t span = kPosInf - bound;
+    refine_output(bound, 0u, span ? 32 - __clz(span) : 0, (uint32_t)a.k2, m,
+                  a.out2 + (int64_t)row * a.k2, a.n_kept2, a.k2);
+  };
+
+
 
   // ---- 0. resident rows: a threshold from a sample ----
   // Two keys per thread, spread over each wave's slice, go through the same
@@ -497,7 +532,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       write_list(0, theta, p);
       __syncthreads();
       const uint32_t span = kall - theta;
-      refine_output(theta, 0u, span ? 32 - __clz(span) : 0, (uint32_t)k, tot);
+      refine_output(theta, 0u, span ? 32 - __clz(span) : 0, (uint32_t)k, tot, out, n_kept, k);
+      if (nest) nested_output(theta, tot);
       return;
     }
   }
@@ -607,9 +643,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
     }
     m = min(m, (uint32_t)kList);
     if (known)
-      refine_output(K, 0u, 0, need, m);
+      refine_output(K, 0u, 0, need, m, out, n_kept, k);
     else
-      refine_output(kmin, (bin - 1u) << shift, shift, need, m);
+      refine_output(kmin, (bin - 1u) << shift, shift, need, m, out, n_kept, k);
+    if (nest) nested_output(floor_key, m);
     return;
   }
 
@@ -745,7 +782,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool g = key[j][e] > Kc, q = key[j][e] == Kc;
-          if (g || (q && qpre < need)) out[gpre + min(qpre, need)] = map_index<MODE>(blk, ib + e) + off;
+          if (g || (q && qpre < need)) {
+            const uint32_t slot = gpre + min(qpre, need);
+            out[slot] = map_index<MODE>(blk, ib + e) + off;
+            // (nested selection: the kept entries, in index order, as a list)
+            if (nest) *reinterpret_cast<uint2*>(&sh.list[2 * slot]) = make_uint2((uint32_t)(ib + e), key[j][e]);
+          }
           gpre += g ? 1u : 0u;
           qpre += q ? 1u : 0u;
         }
@@ -760,36 +802,40 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
     eq_run += etot;
     __syncthreads();
   }
-  if (MODE == MODE_KEYS && tid == 0) a.n_kept[row] = k;
+  if (MODE == MODE_KEYS && tid == 0) n_kept[row] = k;
+  if (nest) nested_output(K, (uint32_t)k);   // the list holds the k kept entries
 }
 
-template <int MODE, int THREADS, bool RESIDENT, bool BF16>
+template <int MODE, int THREADS, bool RESIDENT, bool BF16, bool NEST>
 static void launch_sized(const TopkArgs& a, int rows, bool vec, hipStream_t st) {
   if (vec)
-    hipLaunchKernelGGL((topk_kernel<MODE, true, THREADS, RESIDENT, BF16>), dim3(rows), dim3(THREADS), 0, st, a);
+    hipLaunchKernelGGL((topk_kernel<MODE, true, THREADS, RESIDENT, BF16, NEST>), dim3(rows), dim3(THREADS), 0, st, a);
   else
-    hipLaunchKernelGGL((topk_kernel<MODE, false, THREADS, RESIDENT, BF16>), dim3(rows), dim3(THREADS), 0, st, a);
+    hipLaunchKernelGGL((topk_kernel<MODE, false, THREADS, RESIDENT, BF16, NEST>), dim3(rows), dim3(THREADS), 0, st, a);
 }
 
 // the workgroup size is chosen from the widest row the call can see
-template <int MODE, bool BF16>
+template <int MODE, bool BF16, bool NEST = false>
 static void launch_mode(const TopkArgs& a, int rows, int64_t width, bool vec, hipStream_t st) {
   if (width <= 4 * kWaveSlice)
-    launch_sized<MODE, 256, true, BF16>(a, rows, vec, st);
+    launch_sized<MODE, 256, true, BF16, NEST>(a, rows, vec, st);
   else if (width <= 8 * kWaveSlice)
-    launch_sized<MODE, 512, true, BF16>(a, rows, vec, st);
+    launch_sized<MODE, 512, true, BF16, NEST>(a, rows, vec, st);
   else if (width <= 16 * kWaveSlice)
-    launch_sized<MODE, 1024, true, BF16>(a, rows, vec, st);
+    launch_sized<MODE, 1024, true, BF16, NEST>(a, rows, vec, st);
   else
-    launch_sized<MODE, 1024, false, BF16>(a, rows, vec, st);
+    launch_sized<MODE, 1024, false, BF16, NEST>(a, rows, vec, st);
 }
 
 hipError_t launch_topk(int mode, const void* X, bool bf16, int64_t ld, const int32_t* nvalid,
                        const int32_t* len_for_blocks, int rows, int k, int64_t max_cols,
                        const int32_t* blocks, int kb, const int32_t* pos_offset, int32_t* out,
-                       int32_t* n_kept, hipStream_t st) {
+                       int32_t* n_kept, int k2, int32_t* out2, int32_t* n_kept2, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  TopkArgs a{X, ld, nvalid, len_for_blocks, k, blocks, kb, pos_offset, out, n_kept};
+  TopkArgs a{X, ld, nvalid, len_for_blocks, k, blocks, kb, pos_offset, out, n_kept, k2, out2, n_kept2};
+  // a nested selection keeps the k first-selection entries as an LDS list of
+  // 4 * THREADS entries: at least k / 4 threads
+  if (mode == MODE_KEYS && k2 > 0) max_cols = max(max_cols, (int64_t)8 * k);
   // vector loads (4 elements) need rows aligned to them
   const size_t vbytes = bf16 ? 8 : 16;
   const bool vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(X) % vbytes == 0);
@@ -805,7 +851,12 @@ hipError_t launch_topk(int mode, const void* X, bool bf16, int64_t ld, const int
       case MODE_IDENTITY: launch_mode<MODE_IDENTITY, false>(a, rows, max_cols, vec, st); break;
       case MODE_BLOCKMAP: launch_mode<MODE_BLOCKMAP, false>(a, rows, max_cols, vec, st); break;
       case MODE_GATHER: launch_mode<MODE_GATHER, false>(a, rows, max_cols, vec, st); break;
-      default: launch_mode<MODE_KEYS, false>(a, rows, max_cols, vec, st); break;
+      default:
+        if (k2 > 0)
+          launch_mode<MODE_KEYS, false, true>(a, rows, max_cols, vec, st);
+        else
+          launch_mode<MODE_KEYS, false>(a, rows, max_cols, vec, st);
+        break;
     }
   }
   return hipGetLastError();
