@@ -2,36 +2,50 @@
 
 Stream choreography of the publish/select handoff (sglang PR "dsv4.1:
 candidate indexer library", Summary and review; vLLM decode page,
-CandidateOverlap fork/join; prefill PR, "Level one"):
+CandidateOverlap fork/join; prefill PR, "Level one"), in the
+source_scores="rescore" form (the default for score matrices of 4 GiB and
+more, as in the long chunk):
 
-  main stream   idx_score_dense_keys (source scores and their block keys in
-                one pass; or idx_score_dense) -> event "scores ready"
-  side stream   waits "scores ready"; (idx_amax8_varlen when the keys were
-                not fused,) idx_topk_blocks, idx_expand_candidates, which
-                records table.ready
-  side stream   then the source's own top-k (it reads the table the same
-                stream wrote), recording "source done"
+  main stream   idx_score_dense_keys with no score matrix: the source's block
+                keys only -> event "scores ready"
+  side stream   waits "scores ready"; idx_topk_blocks_nested (the kb best
+                blocks and, nested in them, the k + 1 best),
+                idx_expand_candidates of the kb-block table (records
+                table.ready), then the source's own top-k: expansion of the
+                (k + 1)-block table, the source query's scores at those
+                blocks (idx_score_sparse_paged) and their block-mapped top-k
+                (idx_topk_rows), recording "source done"
   main stream   per consumer idx_score_sparse_paged (waits table.ready inside
                 the call; its query fold runs before that wait) and
                 idx_topk_rows; finally waits "source done".  The source's
-                top-k gathers S from HBM while the first consumer's scores
-                keep the MFMA and VALU busy (long chunk: about 0.1 ms saved).
+                rescoring runs beside the first consumer.
+
+The source's dense top-k lies inside its k + 1 best blocks: a block holding
+one of the k best positions has at most k - 1 blocks above it (ties go to the
+lower id at both levels; the newest block, +inf, is always among them), so
+the top-k over the scores at those blocks equals the dense top-k.  Rescoring
+4104 columns per row costs less than writing and re-reading the 16.6 GB
+score matrix of the long chunk.
+
+source_scores="dense" keeps the score matrix S (idx_score_dense_keys with S):
+the side stream then runs idx_topk_blocks and the expansion, and the source's
+own top-k gathers S at its candidate columns (mode GATHER, when kb >= k + 1)
+or selects over the dense row (mode IDENTITY).
 
 Every table buffer is allocated on the main stream before the fork and
 record_stream'ed to the side stream that writes it, so the caching allocator
 never recycles a buffer that either stream still uses; the consumers' wait on
 table.ready orders every main-stream read after the side stream's writes.
 
-With few rows (decode: fewer rows than CUs) run() also moves the selects to
-a third stream: the source's own top-k and each consumer's top-k run there,
-each behind an event recorded after the scores it reads, while the main
-stream goes on to the next consumer's sparse scores (two score buffers, the
-main stream waiting for the select that last read a buffer before
-rewriting it); the main stream waits for the select stream at the end.  On
-64 decode rows this cut the step from 0.326 to 0.298 ms; on 2048 and 16384
-rows the sparse scores fill the GPU and moving the consumers' selects gains
-nothing (16384 rows: 34.43-34.58 ms against 34.30-34.44 ms), so there they
-stay on the main stream and only the source's top-k moves, as above.
+With few rows (decode: fewer rows than CUs) run() also moves the consumers'
+selects to a third stream: each consumer's top-k runs there behind an event
+recorded after the scores it reads, while the main stream goes on to the next
+consumer's sparse scores (two score buffers, the main stream waiting for the
+select that last read a buffer before rewriting it); the main stream waits
+for the select stream at the end.  On 64 decode rows this cut the step from
+0.326 to 0.298 ms; on 2048 and 16384 rows the sparse scores fill the GPU and
+moving the consumers' selects gains nothing (16384 rows: 34.43-34.58 ms
+against 34.30-34.44 ms), so there they stay on the main stream.
 
 Tail layers (prefill PR, "Tail rows"): the last `tail_layers` consumers
 score only the last tail_len[j] rows of each request j.  The side stream
@@ -41,12 +55,8 @@ the tail table's own ready event), and those consumers wait on it.
 If any call raises inside a block that was forked onto the side or select
 stream, the main stream waits for that stream before the exception leaves
 (vLLM decode page, CandidateOverlap fork/join), so that a graph capture ends
-with every stream joined and reports the real error.
-
-The source's own top-k is taken over its candidate columns (mode GATHER)
-when kb >= k + 1: every block holding one of the k best positions then has at
-most k - 1 blocks above it, so the result equals the dense top-k; otherwise
-the dense row is selected directly (mode IDENTITY).
+with every stream joined and reports the real error.  No call synchronises
+the host, so run() can be captured into one HIP graph (capture()).
 """
 
 from __future__ import annotations
@@ -93,17 +103,25 @@ class Chunk:
 
     # run() overlaps the selects with the next sparse scores up to this many rows
     OVERLAP_MAX_ROWS = 256
+    # the source's top-k by rescoring its top-(k+1) blocks pays off when the
+    # score matrix it avoids is large: long chunk (17.2 GB of S) -1.0 to -1.6 ms
+    # per chunk; prefill (0.5 GB) +0.09 ms and decode (16 MB) +0.02 ms per step,
+    # where writing S costs next to nothing and the nested block select and
+    # the rescoring do not
+    RESCORE_MIN_S_BYTES = 4 << 30
 
     def __init__(self, wl, device="cuda", n_consumers=None, k_source=None, with_offset=True,
                  share_T=True, fused_keys=True, consumer_bf16=False, overlap_selects=None,
-                 source_side=True, tail_layers=0, source_scores="rescore"):
+                 source_side=True, tail_layers=0, source_scores="auto"):
         self.wl = wl
         self.fused_keys = fused_keys
         self.consumer_bf16 = consumer_bf16   # consumers write and select bf16 scores
         self.device = device
         self.R, self.kb, self.kc = wl.rows, wl.kb, wl.kc
         self.k_src = wl.kc if k_source is None else k_source
-        self.ld, self.ldk = wl.ld, wl.ldk
+        # key rows padded to 4 keys, so that the block select reads them with
+        # 16-byte loads whatever the longest row
+        self.ld, self.ldk = wl.ld, (wl.ldk + 3) // 4 * 4
         self.kp = KPool(_dev(wl.pool, torch.uint8, device), _dev(wl.page_table, torch.int32, device))
         off = _dev(wl.req_start, torch.int32, device) if with_offset else None
         self.rows = Rows(_dev(wl.req, torch.int32, device), _dev(wl.lens, torch.int32, device), off)
@@ -111,9 +129,13 @@ class Chunk:
         self.queries = [Query(_dev(L.qv, torch.uint8, device), _dev(L.qs, torch.uint8, device),
                               _dev(L.w, torch.float32, device)) for L in layers]
         # source top-k: "rescore" its top-(k+1) blocks (keys-only dense pass, no
-        # score matrix), or take it from the "dense" score matrix S
-        if source_scores not in ("rescore", "dense"):
-            raise ValueError("source_scores must be 'rescore' or 'dense'")
+        # score matrix), or take it from the "dense" score matrix S; "auto":
+        # rescore when S would take at least RESCORE_MIN_S_BYTES
+        if source_scores not in ("auto", "rescore", "dense"):
+            raise ValueError("source_scores must be 'auto', 'rescore' or 'dense'")
+        if source_scores == "auto":
+            big = self.R * self.ld * 4 >= self.RESCORE_MIN_S_BYTES
+            source_scores = "rescore" if big else "dense"
         self.k2 = self.k_src + 1
         self.rescore = source_scores == "rescore" and fused_keys and self.k2 <= self.kb
         self.S = None if self.rescore else \
@@ -230,11 +252,12 @@ class Chunk:
                 self.source_done.record(self.side)
 
     def source_topk(self, same_stream_as_table=False):
+        """The source's own top-k from S (waits for the table when it reads it,
+        unless it runs on the stream that built the table: a stream never waits
+        on an event it recorded itself, which a graph capture cannot express).
+        With rescoring it was taken in publish(), on the side stream."""
         if self.rescore:
-            return   # taken in publish(), on the side stream
-        """The source's own top-k (waits for the table when it reads it, unless it
-        runs on the stream that built the table: a stream never waits on an event
-        it recorded itself, which a graph capture cannot express)."""
+            return
         if self.kb >= self.k_src + 1:
             if not same_stream_as_table:
                 stream_wait_table(self.table)
