@@ -67,9 +67,14 @@ def build(verbose: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        # IDX_ORACLE_LIBRARY: another build of idx_oracle.c (the sanitizer build
+        # of tests/test_host_sanitizers.py)
+        path = os.environ.get("IDX_ORACLE_LIBRARY")
+        if not path:
+            if not os.path.exists(_LIB_PATH):
+                build()
+            path = _LIB_PATH
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.oracle_e2m1_value.restype = ctypes.c_double

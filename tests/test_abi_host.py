@@ -11,7 +11,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "idx.h")
-LIB = os.path.join(ROOT, "two_level_top_amd", "libidx.so")
+# IDX_LIBRARY: another build of the same library (the sanitizer build of test_host_sanitizers)
+LIB = os.environ.get("IDX_LIBRARY") or os.path.join(ROOT, "two_level_top_amd", "libidx.so")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libidx.so not built")
 

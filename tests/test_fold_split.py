@@ -5,7 +5,9 @@ sum_h (w_h/2)|q_h.k| + q_f.k with the folded query q_f = sum_h (w_h/2) q_h.
 q_f is not an MXFP4 vector; the kernels feed it to the fp4 MFMA as a sum of
 MXFP4 terms found greedily: per 32-element group, scale 2^ceil(log2(max|r|/6))
 and the nearest e2m1 code of every element of the residual r, then r minus
-that term.  The dense scorer uses 8 terms per row, the consumer scorer 16.
+that term.  The fold kernel writes 16 terms per row; both score kernels use
+the first 8 (the dense kernel packs two rows' 8 terms into one 16-row MFMA
+block, the sparse kernel one row's).
 
 These tests restate that split in numpy (independently of the kernel) and
 check, on the query rows of the tiny and long workloads:
