@@ -87,17 +87,18 @@ constexpr uint32_t kCand = 4096;   // register path: keys of the threshold bin
 // resident rows try a sampled list bound first (section 0 of the kernel)
 constexpr bool kSampledBound = true;
 
-template <int THREADS>
+template <int THREADS, bool NEST = false>
 struct TopkShared {
   static constexpr int kList = 4 * THREADS;   // list path: (position, key) pairs
   uint32_t hist[kBins];
+  uint32_t hist2[NEST ? kBins : 1];           // nested select: the second key's histogram
   union {
     uint32_t cand[kCand];
     uint32_t list[2 * kList];
   };
   uint32_t wred[kTopkMaxWaves][2];
   uint32_t wcnt[kTopkMaxWaves][2];
-  uint32_t bcast[4];
+  uint32_t bcast[8];
 };
 
 // u32 image of an fp32 bit pattern, monotone in the value, with -0 and +0 on
@@ -249,6 +250,56 @@ __device__ __forceinline__ int find_bin(Sh& sh, uint32_t rem, uint32_t* above_ou
   return b;
 }
 
+// find_bin on hist and hist2 at once (for ranks rem1 and rem2): both
+// histograms' counts packed in one word (each half at most the list size,
+// < 2^16), one scan.
+template <int THREADS, class Sh>
+__device__ __forceinline__ void find_bin2(Sh& sh, uint32_t rem1, uint32_t rem2, uint32_t* b1,
+                                          uint32_t* above1, uint32_t* b2, uint32_t* above2) {
+  constexpr int W = THREADS / 64;
+  constexpr int BPT = kBins / THREADS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t cb[BPT];
+  uint32_t csum = 0u;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    const int b = kBins - 1 - BPT * tid - q;
+    cb[q] = sh.hist[b] | (sh.hist2[b] << 16);
+    csum += cb[q];
+  }
+  const uint32_t x = wave_incl_scan(csum);
+  if (lane == 63) sh.wcnt[wave][0] = x;
+  __syncthreads();
+  uint32_t before = 0u;
+#pragma unroll
+  for (int w = 0; w < W; ++w) before += w < wave ? sh.wcnt[w][0] : 0u;
+  const uint32_t above = before + x - csum;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int s = 16 * h;
+    const uint32_t rem = h ? rem2 : rem1;
+    const uint32_t a = (above >> s) & 0xffffu, c = (csum >> s) & 0xffffu;
+    if (a < rem && rem <= a + c) {
+      uint32_t acc = a;
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        const uint32_t v = (cb[q] >> s) & 0xffffu;
+        if (acc < rem && rem <= acc + v) {
+          sh.bcast[4 * h] = (uint32_t)(kBins - 1 - BPT * tid - q);
+          sh.bcast[4 * h + 1] = acc;
+        }
+        acc += v;
+      }
+    }
+  }
+  __syncthreads();
+  *b1 = sh.bcast[0];
+  *above1 = sh.bcast[1];
+  *b2 = sh.bcast[4];
+  *above2 = sh.bcast[5];
+  __syncthreads();
+}
+
 // RESIDENT: every row fits one chunk (n <= THREADS * 32), loaded once.
 // NEST (block keys only): also the nested k2 best blocks (a kernel of its own,
 // so that the plain block selection carries none of it)
@@ -257,7 +308,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
   constexpr int W = THREADS / 64;
   constexpr int kChunk = W * kWaveSlice;
   constexpr bool kMapped = MODE == MODE_BLOCKMAP || MODE == MODE_GATHER;
-  using Sh = TopkShared<THREADS>;
+  using Sh = TopkShared<THREADS, NEST>;
   constexpr int kList = Sh::kList;
   __shared__ Sh sh;
   const int row = blockIdx.x;
@@ -381,35 +432,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
     }
   };
 
-  // on the m list entries: fix the bits of K - base below `low` (the bits
-  // above are `fixed`; `need` counts the entries still to take from those
-  // with the fixed high bits), then write the kept entries in list order to
-  // out; kk = the row's selection size (recorded in n_kept for block keys)
-  auto refine_output = [&](uint32_t base, uint32_t fixed, int low, uint32_t need, uint32_t m,
-                           int32_t* out, int32_t* n_kept, int kk) {
-    // ---- 3a. refine the low bits of K on the list ----
-    while (low > 0) {
-      const int width = low < 11 ? low : 11;
-      const int sh_lo = low - width;
-      const uint32_t hi_mask = low >= 32 ? 0u : ~((1u << low) - 1u);
-      for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
-      __syncthreads();
-      for (uint32_t i = tid; i < m; i += THREADS) {
-        const uint32_t r = sh.list[2 * i + 1] - base;
-        if ((r & hi_mask) == fixed) atomicAdd(&sh.hist[(r >> sh_lo) & ((1u << width) - 1u)], 1u);
-      }
-      __syncthreads();
-      uint32_t ab, cnt;
-      const uint32_t d = (uint32_t)find_bin<THREADS>(sh, need, &ab, &cnt);
-      need -= ab;
-      fixed |= d << sh_lo;
-      low = sh_lo;
-    }
-    const uint32_t K = base + fixed;
-
-    // ---- 3b. ordered output from the list ----
-    // thread t takes entries [t E, t E + E); one scan of the packed
-    // (greater << 16 | equal) counts gives every entry its output slot
+  // ---- 3b. ordered output from the list ----
+  // K = the k-th largest key, need = how many entries equal to K are kept:
+  // thread t takes entries [t E, t E + E); one scan of the packed
+  // (greater << 16 | equal) counts gives every entry its output slot; kk =
+  // the row's selection size (recorded in n_kept for block keys)
+  auto ordered_output = [&](uint32_t K, uint32_t need, uint32_t m, int32_t* out, int32_t* n_kept, int kk) {
     const uint32_t E = (m + THREADS - 1) / THREADS;
     const uint32_t s0 = min((uint32_t)tid * E, m), s1 = min(s0 + E, m);
     uint32_t cnt = 0u;
@@ -433,6 +461,67 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       qpre += q ? 1u : 0u;
     }
     if (MODE == MODE_KEYS && tid == 0) n_kept[row] = kk;
+  };
+
+  // ---- 3a. on the m list entries: fix the bits of K - base below `low`
+  // (the bits above are `fixed`; `need` counts the entries still to take
+  // from those with the fixed high bits), 11 bits per histogram pass; then
+  // the ordered output
+  auto refine_output = [&](uint32_t base, uint32_t fixed, int low, uint32_t need, uint32_t m,
+                           int32_t* out, int32_t* n_kept, int kk) {
+    while (low > 0) {
+      const int width = low < 11 ? low : 11;
+      const int sh_lo = low - width;
+      const uint32_t hi_mask = low >= 32 ? 0u : ~((1u << low) - 1u);
+      for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
+      __syncthreads();
+      for (uint32_t i = tid; i < m; i += THREADS) {
+        const uint32_t r = sh.list[2 * i + 1] - base;
+        if ((r & hi_mask) == fixed) atomicAdd(&sh.hist[(r >> sh_lo) & ((1u << width) - 1u)], 1u);
+      }
+      __syncthreads();
+      uint32_t ab, cnt;
+      const uint32_t d = (uint32_t)find_bin<THREADS>(sh, need, &ab, &cnt);
+      need -= ab;
+      fixed |= d << sh_lo;
+      low = sh_lo;
+    }
+    ordered_output(base + fixed, need, m, out, n_kept, kk);
+  };
+
+  // Both selections of a nested row from one list (every entry >= base, the
+  // k best and, nested in them, the k2 best): their keys are refined in the
+  // same passes, one histogram each, then written one after the other.
+  auto refine_dual = [&](uint32_t base, int low, uint32_t m) {
+    uint32_t need1 = (uint32_t)a.k, need2 = (uint32_t)a.k2, fixed1 = 0u, fixed2 = 0u;
+    while (low > 0) {
+      const int width = low < 11 ? low : 11;
+      const int sh_lo = low - width;
+      const uint32_t hi_mask = low >= 32 ? 0u : ~((1u << low) - 1u);
+      const uint32_t msk = (1u << width) - 1u;
+      for (int b = tid; b < kBins; b += THREADS) {
+        sh.hist[b] = 0u;
+        sh.hist2[b] = 0u;
+      }
+      __syncthreads();
+      for (uint32_t i = tid; i < m; i += THREADS) {
+        const uint32_t r = sh.list[2 * i + 1] - base;
+        const uint32_t hi = r & hi_mask, d = (r >> sh_lo) & msk;
+        if (hi == fixed1) atomicAdd(&sh.hist[d], 1u);
+        if (hi == fixed2) atomicAdd(&sh.hist2[d], 1u);
+      }
+      __syncthreads();
+      uint32_t d1, ab1, d2, ab2;
+      find_bin2<THREADS>(sh, need1, need2, &d1, &ab1, &d2, &ab2);
+      need1 -= ab1;
+      need2 -= ab2;
+      fixed1 |= d1 << sh_lo;
+      fixed2 |= d2 << sh_lo;
+      low = sh_lo;
+    }
+    ordered_output(base + fixed1, need1, m, a.out + (int64_t)row * a.k, a.n_kept, a.k);
+    __syncthreads();   // the first output has read the list counts
+    ordered_output(base + fixed2, need2, m, a.out2 + (int64_t)row * a.k2, a.n_kept2, a.k2);
   };
 
   // the k2 best blocks from the list of a first selection: every entry is at
@@ -532,8 +621,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       write_list(0, theta, p);
       __syncthreads();
       const uint32_t span = kall - theta;
+      if constexpr (NEST) {
+        if (nest) {   // (kall >= every list key: the width covers both selections)
+          refine_dual(theta, span ? 32 - __clz(span) : 0, tot);
+          return;
+        }
+      }
       refine_output(theta, 0u, span ? 32 - __clz(span) : 0, (uint32_t)k, tot, out, n_kept, k);
-      if (nest) nested_output(theta, tot);
       return;
     }
   }
