@@ -467,6 +467,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
   // (the bits above are `fixed`; `need` counts the entries still to take
   // from those with the fixed high bits), 11 bits per histogram pass; then
   // the ordered output
+  constexpr bool kRankFinish = MODE == MODE_BLOCKMAP || MODE == MODE_IDENTITY;
   auto refine_output = [&](uint32_t base, uint32_t fixed, int low, uint32_t need, uint32_t m,
                            int32_t* out, int32_t* n_kept, int kk) {
     while (low > 0) {
@@ -474,6 +475,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       const int sh_lo = low - width;
       const uint32_t hi_mask = low >= 32 ? 0u : ~((1u << low) - 1u);
       for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
+      if (tid == 0) sh.bcast[2] = 0u;
       __syncthreads();
       for (uint32_t i = tid; i < m; i += THREADS) {
         const uint32_t r = sh.list[2 * i + 1] - base;
@@ -485,6 +487,36 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       need -= ab;
       fixed |= d << sh_lo;
       low = sh_lo;
+      // (score rows only: in the gathered and nested block selects the extra
+      // code cost more registers than the saved pass gained)
+      if (kRankFinish && low > 0 && cnt <= 64u) {
+        // a few entries left with K's high bits: rank them directly instead
+        // of further passes.  Their keys go to hist[0 .. cnt) (free again
+        // after find_bin); wave w ranks keys w, w + W, ...: key i is K when
+        // fewer than `need` keys are above it and at least `need` at or above
+        // it (each wave compares one key with all of them, one per lane).
+        const uint32_t lo_mask = ~((1u << low) - 1u);
+        for (uint32_t i = tid; i < m; i += THREADS) {
+          const uint32_t x = sh.list[2 * i + 1];
+          if (((x - base) & lo_mask) == fixed) sh.hist[atomicAdd(&sh.bcast[2], 1u)] = x;
+        }
+        __syncthreads();
+        const bool in = lane < (int)cnt;
+        const uint32_t xl = in ? sh.hist[lane] : 0u;
+        for (uint32_t i = wave; i < cnt; i += W) {
+          const uint32_t xi = sh.hist[i];
+          const uint32_t g = (uint32_t)__popcll(__ballot(in && xl > xi));
+          const uint32_t eq = (uint32_t)__popcll(__ballot(in && xl == xi));
+          if (lane == 0 && g < need && need <= g + eq) {   // (equal keys write equal values)
+            sh.bcast[0] = xi;
+            sh.bcast[1] = need - g;
+          }
+        }
+        __syncthreads();
+        const uint32_t K = sh.bcast[0], neq = sh.bcast[1];
+        ordered_output(K, neq, m, out, n_kept, kk);
+        return;
+      }
     }
     ordered_output(base + fixed, need, m, out, n_kept, kk);
   };
