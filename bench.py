@@ -278,6 +278,7 @@ def main():
         s = rec.spans(a, b)
         return float(np.mean(s)) if s else float("nan")
 
+    t_fold = avg("fold<", "fold>") if ch.prefold else float("nan")
     t_dense = avg("dense<", "dense>")
     t_amax = avg("amax8<", "amax8>")
     t_tkb = avg("topk_blocks<", "topk_blocks>")
@@ -289,6 +290,9 @@ def main():
     dense_name = ("score_dense_keys (keys only)" if ch.rescore else "score_dense_keys") \
         if ch.fused_keys else "score_dense"
     kernels = {
+        **({"fold_queries": {"ms": round(t_fold, 4),
+                             "note": "every layer's folded query, one launch at the start of the step"}}
+           if ch.prefold else {}),
         dense_name: {"ms": round(t_dense, 4), "TFLOP/s": round(dense_tflops, 1),
                      "frac_fp4_peak": round(dense_tflops / PEAK_FP4_TFLOPS, 4)},
         **({} if ch.fused_keys else {"amax8_varlen": {

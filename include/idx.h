@@ -79,6 +79,11 @@ const char* idx_version(void);
  *   vals   u8  [rows][heads][64]   packed e2m1 codes
  *   scales u8  [rows][heads][4]    ue8m0 scales
  *   w      f32 [rows][heads]       head weights (already folded upstream)
+ *   folded u8  [rows][1088]        nullable: this batch's weight-folded query
+ *                                  as written by idx_fold_queries; when set,
+ *                                  the score calls read it instead of folding
+ *                                  the query themselves (their ws may then be
+ *                                  NULL).  16-byte aligned.
  * 1 <= heads <= 64 (64 in the model; 8 in small tests); dim must be 128.
  * vals 16-byte, scales and w 4-byte aligned (IDX_E_ALIGN otherwise). */
 typedef struct {
@@ -88,6 +93,7 @@ typedef struct {
   int32_t rows;
   int32_t heads;
   int32_t dim;
+  const uint8_t* folded;
 } idx_query;
 
 /* The paged MXFP4 index-K pool (the vLLM sparse_attn_indexer page,
@@ -162,6 +168,24 @@ enum {
 size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k);
 
 /*
+ * idx_fold_queries -- the weight-folded queries of n query batches (the index
+ * layers of one step) in one launch: ws_host[i] gets batch i's
+ * sum_h (w_h/2) q_h as 16 MXFP4 terms per row (what the score calls otherwise
+ * write into their own workspace first; see idx_score_dense).  Pass
+ * ws_host[i] as q->folded of the later score calls: a step's layers are
+ * independent, so their folds fill the GPU together where one layer's rows
+ * would not (decode), and they leave the critical path between the score
+ * calls.  (The score is the prefill PR's Motivation's sum_h w_h relu(q_h.k),
+ * computed as relu(s) = (s + |s|)/2: the folded query carries the linear half.)
+ *   qs_host       host array of n query descriptors (their `folded` is ignored)
+ *   ws_host       host array of n device pointers, 16-byte aligned
+ *   ws_bytes_host host array: ws_bytes_host[i] >= idx_workspace_bytes(IDX_OP_SCORE, qs_host[i].rows, 0, 0)
+ * 1 <= n <= 16.
+ */
+idx_status idx_fold_queries(const idx_query* qs_host, int32_t n, void* const* ws_host,
+                            const size_t* ws_bytes_host, hipStream_t stream);
+
+/*
  * idx_score_dense -- the source layer's dense scores.
  * Prefill PR, Motivation: the fp32 [tokens, context] score matrix that the
  * source scores in full; vLLM indexer page: fp8_fp4_mqa_logits over
@@ -172,7 +196,8 @@ size_t idx_workspace_bytes(int op, int32_t rows, int64_t width, int32_t k);
  * ws: idx_workspace_bytes(IDX_OP_SCORE, q->rows, 0, 0) device bytes, 16-byte
  * aligned; the call first writes there each row's weight-folded query
  * sum_h (w_h/2) q_h as 16 MXFP4 terms (exact), which lets the kernel use
- * relu(s) = (s + |s|)/2 with the linear half on the MFMA.
+ * relu(s) = (s + |s|)/2 with the linear half on the MFMA.  With q->folded
+ * set, the call reads the folded query there instead and ws is unused.
  */
 idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows,
                            float* S, int64_t ld, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -311,7 +336,8 @@ idx_status idx_score_sparse_paged(const idx_query* q, const idx_kpool* kp, const
  * argument.  Same arguments, results (bit for bit) and errors otherwise.
  *   q->rows <= 4096 (else IDX_E_UNSUPPORTED, nothing enqueued): the scratch
  *   holds 4096 rows x 1088 bytes (4.25 MiB), one copy per GPU, held until
- *   the process ends.
+ *   the process ends.  With q->folded set the scratch is not used and the
+ *   row limit does not apply.
  * The first call on a device looks the scratch address up with that device
  * current (make that first call outside a graph capture).  Every call on a
  * GPU shares that GPU's scratch, which keeps the last call's contents (each

@@ -190,3 +190,28 @@ def test_workspace_sizes(lib):
     assert lib.idx_workspace_bytes(4, 100, 0, 0) == (2 * 100 + 1) * 4 + 12   # 16-byte multiple
     assert lib.idx_workspace_bytes(1, 100, 32768, 2048) == 0
     assert lib.idx_workspace_bytes(5, 100, 0, 0) == 100 * 1088
+
+
+def test_fold_queries_validation(lib):
+    t, q, kp, rows, tbl = _structs()
+    P = ctypes.byref
+    f = lib.idx_fold_queries
+    qs = (t._Query * 2)(q, q)
+    ws = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    W = 1 << 20
+    sizes = (ctypes.c_size_t * 2)(W, W)
+    assert f(qs, 0, ws, sizes, None) == -1                      # n < 1
+    assert f(qs, 17, ws, sizes, None) == -1                     # n > 16
+    assert "1..16" in _err(lib)
+    assert f(None, 2, ws, sizes, None) == -1
+    assert f(qs, 2, None, sizes, None) == -1
+    small = (ctypes.c_size_t * 2)(W, 100)
+    assert f(qs, 2, ws, small, None) == -6                      # workspace of batch 1
+    odd = (ctypes.c_void_p * 2)(FAKE, FAKE_ODD)
+    assert f(qs, 2, odd, sizes, None) == -2                     # 16-byte alignment
+    bad = (t._Query * 2)(q, t._Query(FAKE, FAKE, FAKE, 4, 64, 64))
+    assert f(bad, 2, ws, sizes, None) == -4                     # dim of batch 1
+    # a folded query replaces the workspace of the score calls, and must be aligned
+    qf = t._Query(FAKE, FAKE, FAKE, 4, 64, 128, FAKE_ODD)
+    assert lib.idx_score_dense(P(qf), P(kp), P(rows), FAKE, 1024, None, 0, None) == -2
+    assert "folded" in _err(lib)

@@ -888,6 +888,50 @@ def test_keys_only_pass_matches_keys_with_scores(idx):
             assert bool((k1 == k2).all()), f"{wl.name} skip={skip}"
 
 
+def test_fold_queries_bitexact(idx):
+    """idx_fold_queries writes, for several query batches in one launch, the same
+    folded queries as each score call's own fold into its workspace."""
+    from two_level_top_amd.chunk import Chunk
+    wls = [workloads.tiny(), workloads.decode(n_consumers=1), _fused_case("ragged24")[0]]
+    qs, ref = [], []
+    for wl in wls:
+        ch = Chunk(wl, n_consumers=0, source_scores="dense", prefold=False)
+        for L in wl.layers[:2]:
+            q = idx.Query(dev(L.qv), dev(L.qs), dev(L.w))
+            ws = idx.score_workspace(wl.rows)
+            S = torch.empty((wl.rows, wl.ld), dtype=torch.float32, device="cuda")
+            idx.idx_score_dense(q, ch.kp, ch.rows, S, ws=ws)
+            qs.append(q)
+            ref.append(host(ws)[: wl.rows * 1088])
+    say(f"fold queries: {len(qs)} batches in one launch")
+    out = [torch.full((max(16, q.rows * 1088),), 0xAB, dtype=torch.uint8, device="cuda") for q in qs]
+    idx.idx_fold_queries(qs, out)
+    for i, (o, r) in enumerate(zip(out, ref)):
+        assert np.array_equal(host(o)[: len(r)], r), f"batch {i}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "decode_mtp"])
+def test_chunk_prefold_matches_call_folds(idx, name):
+    """A chunk that folds every layer's query in one launch first gives the same
+    outputs, bit for bit, as one whose score calls fold their own queries."""
+    from two_level_top_amd.chunk import Chunk
+    wl = {"tiny": workloads.tiny, "decode": workloads.decode, "decode_mtp": workloads.decode_mtp}[name]()
+    say(f"prefold chunk {name}")
+    outs = []
+    for prefold in (False, True):
+        for source in ("rescore", "dense"):
+            ch = Chunk(wl, source_scores=source, prefold=prefold)
+            ch.run()
+            outs.append((prefold, source, host(ch.src_top), [host(c) for c in ch.cons_top],
+                         host(ch.table.blocks)))
+    for source in ("rescore", "dense"):
+        a = [o for o in outs if o[1] == source and not o[0]][0]
+        b = [o for o in outs if o[1] == source and o[0]][0]
+        assert np.array_equal(a[2], b[2]), f"{name} {source}: source top-k"
+        assert all(np.array_equal(x, y) for x, y in zip(a[3], b[3])), f"{name} {source}: consumers"
+        assert np.array_equal(a[4], b[4]), f"{name} {source}: blocks"
+
+
 def test_chunk_decode_overlap_matches_serial(idx):
     """Few rows run the selects on their own stream, behind the next consumer's
     scores, with two score buffers reused across 4 consumers; the outputs are

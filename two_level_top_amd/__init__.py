@@ -50,7 +50,7 @@ _I64 = ctypes.c_int64
 
 class _Query(ctypes.Structure):
     _fields_ = [("vals", _P), ("scales", _P), ("w", _P), ("rows", _I32), ("heads", _I32),
-                ("dim", _I32)]
+                ("dim", _I32), ("folded", _P)]
 
 
 class _KPool(ctypes.Structure):
@@ -95,6 +95,7 @@ def load():
         "idx_score_sparse_paged_bf16": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P, ctypes.c_size_t, _P],
         "idx_prefill_tail": [ctypes.POINTER(_Table), _P, _P, _I32, ctypes.POINTER(_Table), _P, ctypes.c_size_t, _P],
         "idx_score_sparse_paged_noalloc": [ctypes.POINTER(_Query), ctypes.POINTER(_KPool), ctypes.POINTER(_Table), _P, _I64, _P],
+        "idx_fold_queries": [ctypes.POINTER(_Query), _I32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_size_t), _P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -183,9 +184,12 @@ def _width(t: torch.Tensor, need: int, name: str):
 # ---------------------------------------------------------------------------
 
 class Query:
-    """One index layer's query batch: vals u8 [R,H,64], scales u8 [R,H,4], w f32 [R,H]."""
+    """One index layer's query batch: vals u8 [R,H,64], scales u8 [R,H,4], w f32 [R,H].
+    `folded`: None, or a workspace that idx_fold_queries filled with this batch's
+    folded query; the score calls then read it instead of folding themselves."""
 
     def __init__(self, vals, scales, w):
+        self.folded = None
         self.vals = _req(vals, torch.uint8, "vals", gpu=False)
         self.scales = _req(scales, torch.uint8, "scales", gpu=False)
         self.w = _req(w, torch.float32, "w", gpu=False)
@@ -198,7 +202,13 @@ class Query:
         _on_gpu(self.vals, self.scales, self.w, names=("vals", "scales", "w"))
 
     def c(self):
-        return _Query(_ptr(self.vals), _ptr(self.scales), _ptr(self.w), self.rows, self.heads, 128)
+        folded = None
+        if self.folded is not None:
+            folded = _req(self.folded, torch.uint8, "folded")
+            if folded.numel() < idx_workspace_bytes(OP_SCORE, self.rows, 0, 0):
+                raise IdxError("folded: smaller than the query's fold workspace")
+        return _Query(_ptr(self.vals), _ptr(self.scales), _ptr(self.w), self.rows, self.heads, 128,
+                      _ptr(folded))
 
 
 class KPool:
@@ -295,7 +305,31 @@ def score_workspace(rows: int, device="cuda") -> torch.Tensor:
     return torch.empty((n,), dtype=torch.uint8, device=device)
 
 
-def _score_ws(ws, rows, device, stream):
+def idx_fold_queries(queries, workspaces, stream=None):
+    """The folded queries of several query batches in one launch: workspaces[i]
+    (score_workspace(queries[i].rows)) gets batch i's; set queries[i].folded to it
+    for the score calls that follow."""
+    n = len(queries)
+    if n != len(workspaces) or not 1 <= n <= 16:
+        raise IdxError("idx_fold_queries: 1..16 queries, one workspace each")
+    qs = (_Query * n)(*[q.c() for q in queries])
+    ws = [_req(w, torch.uint8, "ws") for w in workspaces]
+    for q, w in zip(queries, ws):
+        if w.numel() < idx_workspace_bytes(OP_SCORE, q.rows, 0, 0):
+            raise IdxError("idx_fold_queries: workspace too small")
+        _on_gpu(q.vals, w, names=("vals", "ws"))
+    ptrs = (_P * n)(*[_ptr(w) for w in ws])
+    sizes = (ctypes.c_size_t * n)(*[w.numel() for w in ws])
+    _check(load().idx_fold_queries(qs, n, ptrs, sizes, _stream(stream)), "idx_fold_queries")
+
+
+def _numel(t):
+    return 0 if t is None else t.numel()
+
+
+def _score_ws(ws, rows, device, stream, q=None):
+    if q is not None and q.folded is not None:
+        return None   # the folded query is read from q.folded
     if ws is None:
         ws = score_workspace(rows, device)
         if stream is not None:
@@ -307,10 +341,10 @@ def idx_score_dense(q: Query, kp: KPool, rows: Rows, S: torch.Tensor, ws=None, s
     if q.rows != rows.rows:
         raise IdxError(f"query rows {q.rows} != rows {rows.rows}")
     _req(S, torch.float32, "S", rows=rows.rows)
-    ws = _score_ws(ws, q.rows, S.device, stream)
+    ws = _score_ws(ws, q.rows, S.device, stream, q)
     q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
     _check(load().idx_score_dense(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
-                                  _ptr(S), S.stride(0), _ptr(ws), ws.numel(), _stream(stream)),
+                                  _ptr(S), S.stride(0), _ptr(ws), _numel(ws), _stream(stream)),
            "idx_score_dense")
 
 
@@ -327,11 +361,11 @@ def idx_score_dense_keys(q: Query, kp: KPool, rows: Rows, S: torch.Tensor | None
         raise IdxError("keys only (S=None) needs ld")
     _req(keys, torch.float32, "keys", rows=rows.rows, gpu=False)
     _on_gpu(S, keys, names=("S", "keys"))
-    ws = _score_ws(ws, q.rows, keys.device, stream)
+    ws = _score_ws(ws, q.rows, keys.device, stream, q)
     q_c, kp_c, rows_c = q.c(), kp.c(), rows.c()
     _check(load().idx_score_dense_keys(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(rows_c),
                                        _ptr(S), int(ld), _ptr(keys), keys.stride(0),
-                                       int(skip_le_blocks), _ptr(ws), ws.numel(), _stream(stream)),
+                                       int(skip_le_blocks), _ptr(ws), _numel(ws), _stream(stream)),
            "idx_score_dense_keys")
 
 
@@ -427,12 +461,12 @@ def idx_score_sparse_paged(q: Query, kp: KPool, tbl: Table, T: torch.Tensor, ws=
     """wait_ready=False: the call runs on the stream that built the table, so it does
     not wait on the table's ready event (a stream never waits on an event it recorded)."""
     _sparse_args(q, tbl, T, torch.float32)
-    ws = _score_ws(ws, q.rows, T.device, stream)
+    ws = _score_ws(ws, q.rows, T.device, stream, q)
     q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
     if not wait_ready:
         t_c.ready = None
     _check(load().idx_score_sparse_paged(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
-                                         _ptr(T), T.stride(0), _ptr(ws), ws.numel(),
+                                         _ptr(T), T.stride(0), _ptr(ws), _numel(ws),
                                          _stream(stream)),
            "idx_score_sparse_paged")
 
@@ -452,10 +486,10 @@ def idx_score_sparse_paged_bf16(q: Query, kp: KPool, tbl: Table, T: torch.Tensor
                                 stream=None):
     """T: torch.bfloat16 [rows, >= kb * 8]."""
     _sparse_args(q, tbl, T, torch.bfloat16)
-    ws = _score_ws(ws, q.rows, T.device, stream)
+    ws = _score_ws(ws, q.rows, T.device, stream, q)
     q_c, kp_c, t_c = q.c(), kp.c(), tbl.c()
     _check(load().idx_score_sparse_paged_bf16(ctypes.byref(q_c), ctypes.byref(kp_c), ctypes.byref(t_c),
-                                              _ptr(T), T.stride(0), _ptr(ws), ws.numel(),
+                                              _ptr(T), T.stride(0), _ptr(ws), _numel(ws),
                                               _stream(stream)),
            "idx_score_sparse_paged_bf16")
 

@@ -62,12 +62,14 @@ the host, so run() can be captured into one HIP graph (capture()).
 from __future__ import annotations
 
 import contextlib
+import copy
 
 import numpy as np
 import torch
 
 from . import (COLS_BLOCKMAP, COLS_GATHER, COLS_IDENTITY, KPool, Query, Rows, Table,
-               idx_amax8_varlen, idx_expand_candidates, idx_prefill_tail, idx_score_dense,
+               idx_amax8_varlen, idx_expand_candidates, idx_fold_queries, idx_prefill_tail,
+               idx_score_dense,
                idx_score_dense_keys, idx_score_sparse_paged, idx_score_sparse_paged_bf16,
                idx_topk_blocks, idx_topk_blocks_nested, idx_topk_rows, idx_topk_rows_bf16,
                score_workspace, stream_wait_table, tail_workspace)
@@ -112,7 +114,7 @@ class Chunk:
 
     def __init__(self, wl, device="cuda", n_consumers=None, k_source=None, with_offset=True,
                  share_T=True, fused_keys=True, consumer_bf16=False, overlap_selects=None,
-                 source_side=True, tail_layers=0, source_scores="auto"):
+                 source_side=True, tail_layers=0, source_scores="auto", prefold=True):
         self.wl = wl
         self.fused_keys = fused_keys
         self.consumer_bf16 = consumer_bf16   # consumers write and select bf16 scores
@@ -174,6 +176,20 @@ class Chunk:
         self.cons_top = [torch.empty((self.R if not self._is_tail(i) else len(self.tail_rows), self.kc),
                                      dtype=torch.int32, device=device) for i in range(ncons)]
         self.ws = score_workspace(self.R, device)      # folded queries of the layer being scored
+        # prefold: every layer's folded query in one launch at the start of the
+        # step (idx_fold_queries), which the score calls then read
+        # (self.queries stay as given; the score calls use self.fq, copies that
+        # carry the folded workspaces)
+        self.prefold = prefold
+        self.fold_ws = []
+        self.fq = list(self.queries)
+        if prefold:
+            self.fold_ws = [score_workspace(q.rows, device) for q in self.queries]
+            self.fq = []
+            for q, w in zip(self.queries, self.fold_ws):
+                f = copy.copy(q)
+                f.folded = w
+                self.fq.append(f)
         self.side = torch.cuda.Stream(device=device)
         self.scores_ready = torch.cuda.Event()
         self.sel = torch.cuda.Stream(device=device) if self.overlap else None
@@ -192,16 +208,23 @@ class Chunk:
             self.recorder.mark(name)
 
     # -- the source layer ---------------------------------------------------
+    def fold(self, stream=None):
+        """All layers' folded queries in one launch (prefold)."""
+        if self.prefold:
+            self._mark("fold<")
+            idx_fold_queries(self.queries, self.fold_ws, stream=stream)
+            self._mark("fold>")
+
     def score_source(self, stream=None):
         self._mark("dense<")
         if self.rescore:   # keys only; rows with more than k + 1 blocks are keyed
-            idx_score_dense_keys(self.queries[0], self.kp, self.rows, None, self.keys,
+            idx_score_dense_keys(self.fq[0], self.kp, self.rows, None, self.keys,
                                  skip_le_blocks=self.k2, ws=self.ws, stream=stream, ld=self.ld)
         elif self.fused_keys:
-            idx_score_dense_keys(self.queries[0], self.kp, self.rows, self.S, self.keys,
+            idx_score_dense_keys(self.fq[0], self.kp, self.rows, self.S, self.keys,
                                  skip_le_blocks=self.kb, ws=self.ws, stream=stream)
         else:
-            idx_score_dense(self.queries[0], self.kp, self.rows, self.S, ws=self.ws, stream=stream)
+            idx_score_dense(self.fq[0], self.kp, self.rows, self.S, ws=self.ws, stream=stream)
         self._mark("dense>")
 
     def publish(self):
@@ -243,7 +266,7 @@ class Chunk:
                 # consumers start on table.ready meanwhile)
                 idx_expand_candidates(self.kp, self.rows, self.table2)
                 self._mark("source_topk<")
-                idx_score_sparse_paged(self.queries[0], self.kp, self.table2, self.T_src, ws=self.ws_src,
+                idx_score_sparse_paged(self.fq[0], self.kp, self.table2, self.T_src, ws=self.ws_src,
                                        wait_ready=False)
                 idx_topk_rows(self.T_src, self.table2.valid_len, self.k_src, self.src_top,
                               mode=COLS_BLOCKMAP, blocks=self.table2.blocks,
@@ -281,7 +304,7 @@ class Chunk:
         score = idx_score_sparse_paged_bf16 if self.consumer_bf16 else idx_score_sparse_paged
         tbl, _, T_own = self._layer_table(i)
         self._mark(f"sparse{i}<")
-        score(self.queries[1 + i], self.kp, tbl, T if T_own is None else T_own, ws=self.ws)
+        score(self.fq[1 + i], self.kp, tbl, T if T_own is None else T_own, ws=self.ws)
         self._mark(f"sparse{i}>")
 
     def _select(self, i: int, T):
@@ -302,6 +325,7 @@ class Chunk:
         (the selects on their own stream when overlap is on; the current stream
         waits for them before returning)."""
         main = torch.cuda.current_stream()
+        self.fold()
         self.score_source()
         self.publish()
         try:

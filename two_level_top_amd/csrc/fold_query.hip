@@ -52,13 +52,28 @@ __device__ __forceinline__ double code_value2(int c) {
   return (double)((c & 8) ? -m2 : m2);
 }
 
-__global__ __launch_bounds__(256) void fold_query_kernel(QueryArgs q, uint8_t* __restrict__ out) {
+// Several query batches (index layers) folded in one launch: workgroups
+// [wg0[i], wg0[i + 1]) take batch i.  A step's layers are independent of each
+// other, so folding them together fills the GPU where one layer's rows would
+// not (decode: 64 rows = 16 workgroups per layer).
+struct FoldBatch {
+  QueryArgs q[kMaxFoldBatches];
+  uint8_t* out[kMaxFoldBatches];
+  int wg0[kMaxFoldBatches + 1];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void fold_query_kernel(FoldBatch fb) {
   __shared__ uint4 stage[kFoldRowsPerWG][kFoldMaxHeads * kValBytes / 16];
   __shared__ double hscale[kFoldRowsPerWG][kFoldMaxHeads * 4];
   __shared__ double2 pair[256];
+  int bi = 0;   // this workgroup's batch (uniform)
+  while (bi + 1 < fb.n && (int)blockIdx.x >= fb.wg0[bi + 1]) ++bi;
+  const QueryArgs q = fb.q[bi];
+  uint8_t* __restrict__ out = fb.out[bi];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int row = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * kFoldRowsPerWG + wave));
+  const int row = __builtin_amdgcn_readfirstlane((int)((blockIdx.x - fb.wg0[bi]) * kFoldRowsPerWG + wave));
   const bool live = row < q.rows;
   const int rr = live ? row : q.rows - 1;   // a dead wave computes a copy and stores nothing
   const int H = q.heads;
@@ -126,11 +141,26 @@ __global__ __launch_bounds__(256) void fold_query_kernel(QueryArgs q, uint8_t* _
   }
 }
 
-hipError_t launch_fold_query(const QueryArgs& q, uint8_t* out, hipStream_t st) {
-  if (q.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fold_query_kernel, dim3((q.rows + kFoldRowsPerWG - 1) / kFoldRowsPerWG), dim3(256), 0,
-                     st, q, out);
+hipError_t launch_fold_queries(const QueryArgs* q, uint8_t* const* out, int n, hipStream_t st) {
+  FoldBatch fb{};
+  int wg = 0;
+  fb.n = 0;
+  for (int i = 0; i < n; ++i) {
+    if (q[i].rows <= 0) continue;
+    fb.q[fb.n] = q[i];
+    fb.out[fb.n] = out[i];
+    fb.wg0[fb.n] = wg;
+    wg += (q[i].rows + kFoldRowsPerWG - 1) / kFoldRowsPerWG;
+    ++fb.n;
+  }
+  fb.wg0[fb.n] = wg;
+  if (wg == 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_query_kernel, dim3(wg), dim3(256), 0, st, fb);
   return hipGetLastError();
+}
+
+hipError_t launch_fold_query(const QueryArgs& q, uint8_t* out, hipStream_t st) {
+  return launch_fold_queries(&q, &out, 1, st);
 }
 
 }  // namespace idxk

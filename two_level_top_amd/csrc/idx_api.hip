@@ -44,6 +44,7 @@ idx_status check_query(const idx_query* q, const char* fn) {
   if (!aligned(q->vals, 16)) return fail(IDX_E_ALIGN, "%s: query vals must be 16-byte aligned", fn);
   if (!aligned(q->scales, 4)) return fail(IDX_E_ALIGN, "%s: query scales must be 4-byte aligned", fn);
   if (!aligned(q->w, 4)) return fail(IDX_E_ALIGN, "%s: query w must be 4-byte aligned", fn);
+  if (!aligned(q->folded, 16)) return fail(IDX_E_ALIGN, "%s: folded query must be 16-byte aligned", fn);
   return IDX_OK;
 }
 
@@ -188,14 +189,36 @@ static idx_status score_dense_impl(const idx_query* q, const idx_kpool* kp, cons
   if (!S && !keys) return fail(IDX_E_ARG, "%s: S is NULL", fn);   // (keys only: S may be NULL)
   if (!aligned(S, 4)) return fail(IDX_E_ALIGN, "%s: S must be 4-byte aligned", fn);
   if (keys && !aligned(keys, 4)) return fail(IDX_E_ALIGN, "%s: keys must be 4-byte aligned", fn);
-  TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
   idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
   idxk::PoolArgs pa{kp->pool, kp->num_pages, kp->page_table, kp->num_req, kp->max_pages};
-  uint8_t* fold = static_cast<uint8_t*>(ws);
-  hipError_t e = idxk::launch_fold_query(qa, fold, stream);
-  if (e != hipSuccess) return hip_status(e, fn);
+  const uint8_t* fold = q->folded;
+  if (!fold) {   // fold the query first, into the workspace
+    TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
+    uint8_t* out = static_cast<uint8_t*>(ws);
+    hipError_t e = idxk::launch_fold_query(qa, out, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+    fold = out;
+  }
   return hip_status(idxk::launch_score_dense(qa, fold, pa, rows->req, rows->len, S, ld, keys, ldk,
                                              skip, stream), fn);
+}
+
+idx_status idx_fold_queries(const idx_query* qs_host, int32_t n, void* const* ws_host,
+                            const size_t* ws_bytes_host, hipStream_t stream) {
+  const char* fn = "idx_fold_queries";
+  if (n < 1 || n > idxk::kMaxFoldBatches)
+    return fail(IDX_E_ARG, "%s: n = %d (1..%d)", fn, n, idxk::kMaxFoldBatches);
+  if (!qs_host || !ws_host || !ws_bytes_host) return fail(IDX_E_ARG, "%s: NULL host array", fn);
+  idxk::QueryArgs qa[idxk::kMaxFoldBatches];
+  uint8_t* out[idxk::kMaxFoldBatches];
+  for (int i = 0; i < n; ++i) {
+    TRY(check_query(&qs_host[i], fn));
+    TRY(check_score_ws(ws_host[i], ws_bytes_host[i], qs_host[i].rows, fn));
+    qa[i] = idxk::QueryArgs{qs_host[i].vals, qs_host[i].scales, qs_host[i].w, qs_host[i].rows,
+                            qs_host[i].heads};
+    out[i] = static_cast<uint8_t*>(ws_host[i]);
+  }
+  return hip_status(idxk::launch_fold_queries(qa, out, n, stream), fn);
 }
 
 idx_status idx_score_dense(const idx_query* q, const idx_kpool* kp, const idx_rows* rows, float* S,
@@ -314,14 +337,18 @@ static idx_status score_sparse_impl(const idx_query* q, const idx_kpool* kp, con
     return fail(IDX_E_UNSUPPORTED, "%s: pool of %d pages exceeds 4 GiB", fn, kp->num_pages);
   if (tbl->rows > 0 && !T) return fail(IDX_E_ARG, "%s: T is NULL", fn);
   if (!aligned(T, bf16 ? 2 : 4)) return fail(IDX_E_ALIGN, "%s: T must be %d-byte aligned", fn, bf16 ? 2 : 4);
-  TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
   // the query fold reads only the query: it is enqueued before the wait on
   // the table, so it can run while the table is still being built
   idxk::QueryArgs qa{q->vals, q->scales, q->w, q->rows, q->heads};
-  uint8_t* fold = static_cast<uint8_t*>(ws);
-  if (tbl->rows > 0) {
-    hipError_t e = idxk::launch_fold_query(qa, fold, stream);
-    if (e != hipSuccess) return hip_status(e, fn);
+  const uint8_t* fold = q->folded;
+  if (!fold) {
+    TRY(check_score_ws(ws, ws_bytes, q->rows, fn));
+    uint8_t* out = static_cast<uint8_t*>(ws);
+    if (tbl->rows > 0) {
+      hipError_t e = idxk::launch_fold_query(qa, out, stream);
+      if (e != hipSuccess) return hip_status(e, fn);
+    }
+    fold = out;
   }
   if (tbl->ready) {
     hipError_t e = hipStreamWaitEvent(stream, tbl->ready, 0);
@@ -344,11 +371,13 @@ idx_status idx_score_sparse_paged_noalloc(const idx_query* q, const idx_kpool* k
                                           hipStream_t stream) {
   const char* fn = "idx_score_sparse_paged_noalloc";
   if (!q) return fail(IDX_E_ARG, "%s: query is NULL", fn);
-  if (q->rows > idxk::kNoAllocMaxRows)
-    return fail(IDX_E_UNSUPPORTED, "%s: %d query rows above the %d rows of the static scratch", fn,
-                q->rows, idxk::kNoAllocMaxRows);
   void* ws = nullptr;
-  if (q->rows > 0) TRY(scratch_address(&ws, fn));
+  if (!q->folded) {   // (a folded query needs no scratch)
+    if (q->rows > idxk::kNoAllocMaxRows)
+      return fail(IDX_E_UNSUPPORTED, "%s: %d query rows above the %d rows of the static scratch", fn,
+                  q->rows, idxk::kNoAllocMaxRows);
+    if (q->rows > 0) TRY(scratch_address(&ws, fn));
+  }
   return score_sparse_impl(q, kp, tbl, T, ld, false, ws, sizeof(idxk::scratch), stream, fn);
 }
 

@@ -42,8 +42,11 @@ __device__ __forceinline__ int clamp_req(int r, int num_req) {
   return r < 0 ? 0 : (r >= num_req ? num_req - 1 : r);
 }
 
-// writes kFoldRowBytes per query row (see fold_query.hip)
+// writes kFoldRowBytes per query row (see fold_query.hip); the batched form
+// folds up to kMaxFoldBatches query batches in one launch
+constexpr int kMaxFoldBatches = 16;
 hipError_t launch_fold_query(const QueryArgs& q, uint8_t* out, hipStream_t st);
+hipError_t launch_fold_queries(const QueryArgs* q, uint8_t* const* out, int n, hipStream_t st);
 
 // keys == nullptr: scores only; otherwise also the block keys of
 // idx_amax8_varlen(S, ld, len, rows, keys, ldk, skip).
