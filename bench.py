@@ -291,7 +291,8 @@ def main():
         if ch.fused_keys else "score_dense"
     kernels = {
         **({"fold_queries": {"ms": round(t_fold, 4),
-                             "note": "every layer's folded query, one launch at the start of the step"}}
+                             "note": "the source layer's folded query (the consumers' are folded in "
+                                     "one launch beside the block select)"}}
            if ch.prefold else {}),
         dense_name: {"ms": round(t_dense, 4), "TFLOP/s": round(dense_tflops, 1),
                      "frac_fp4_peak": round(dense_tflops / PEAK_FP4_TFLOPS, 4)},

@@ -903,11 +903,17 @@ def test_fold_queries_bitexact(idx):
             idx.idx_score_dense(q, ch.kp, ch.rows, S, ws=ws)
             qs.append(q)
             ref.append(host(ws)[: wl.rows * 1088])
+    # an empty batch in the middle folds nothing and shifts nothing
+    L = wls[0].layers[0]
+    empty = idx.Query(dev(L.qv[:0]), dev(L.qs[:0]), dev(L.w[:0]))
+    qs.insert(2, empty)
+    ref.insert(2, np.zeros((0,), dtype=np.uint8))
     say(f"fold queries: {len(qs)} batches in one launch")
     out = [torch.full((max(16, q.rows * 1088),), 0xAB, dtype=torch.uint8, device="cuda") for q in qs]
     idx.idx_fold_queries(qs, out)
     for i, (o, r) in enumerate(zip(out, ref)):
         assert np.array_equal(host(o)[: len(r)], r), f"batch {i}"
+    assert (host(out[2]) == 0xAB).all(), "the empty batch's workspace was written"
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "decode_mtp"])

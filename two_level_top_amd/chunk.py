@@ -6,8 +6,9 @@ CandidateOverlap fork/join; prefill PR, "Level one"), in the
 source_scores="rescore" form (the default for score matrices of 4 GiB and
 more, as in the long chunk):
 
-  main stream   idx_score_dense_keys with no score matrix: the source's block
-                keys only -> event "scores ready"
+  main stream   idx_fold_queries (the source query), idx_score_dense_keys with
+                no score matrix: the source's block keys only -> event
+                "scores ready"
   side stream   waits "scores ready"; idx_topk_blocks_nested (the kb best
                 blocks and, nested in them, the k + 1 best),
                 idx_expand_candidates of the kb-block table (records
@@ -15,10 +16,11 @@ more, as in the long chunk):
                 (k + 1)-block table, the source query's scores at those
                 blocks (idx_score_sparse_paged) and their block-mapped top-k
                 (idx_topk_rows), recording "source done"
-  main stream   per consumer idx_score_sparse_paged (waits table.ready inside
-                the call; its query fold runs before that wait) and
-                idx_topk_rows; finally waits "source done".  The source's
-                rescoring runs beside the first consumer.
+  main stream   idx_fold_queries (all consumer queries, one launch, beside the
+                block select), then per consumer idx_score_sparse_paged
+                (waits table.ready inside the call) and idx_topk_rows;
+                finally waits "source done".  The source's rescoring runs
+                beside the first consumer.
 
 The source's dense top-k lies inside its k + 1 best blocks: a block holding
 one of the k best positions has at most k - 1 blocks above it (ties go to the
@@ -176,8 +178,9 @@ class Chunk:
         self.cons_top = [torch.empty((self.R if not self._is_tail(i) else len(self.tail_rows), self.kc),
                                      dtype=torch.int32, device=device) for i in range(ncons)]
         self.ws = score_workspace(self.R, device)      # folded queries of the layer being scored
-        # prefold: every layer's folded query in one launch at the start of the
-        # step (idx_fold_queries), which the score calls then read
+        # prefold: the layers' folded queries made by idx_fold_queries (the
+        # source's first, the consumers' in one launch beside the block
+        # select), which the score calls then read
         # (self.queries stay as given; the score calls use self.fq, copies that
         # carry the folded workspaces)
         self.prefold = prefold
@@ -208,12 +211,13 @@ class Chunk:
             self.recorder.mark(name)
 
     # -- the source layer ---------------------------------------------------
-    def fold(self, stream=None):
-        """All layers' folded queries in one launch (prefold)."""
-        if self.prefold:
-            self._mark("fold<")
-            idx_fold_queries(self.queries, self.fold_ws, stream=stream)
-            self._mark("fold>")
+    def fold(self, layers, stream=None):
+        """The folded queries of some layers in one launch (prefold): the source's
+        before its dense pass; the consumers' right after the fork of the
+        publish, so that it runs beside the block select on the side stream."""
+        if self.prefold and layers:
+            idx_fold_queries([self.queries[i] for i in layers], [self.fold_ws[i] for i in layers],
+                             stream=stream)
 
     def score_source(self, stream=None):
         self._mark("dense<")
@@ -325,10 +329,13 @@ class Chunk:
         (the selects on their own stream when overlap is on; the current stream
         waits for them before returning)."""
         main = torch.cuda.current_stream()
-        self.fold()
+        self._mark("fold<")
+        self.fold([0])
+        self._mark("fold>")
         self.score_source()
         self.publish()
         try:
+            self.fold(list(range(1, len(self.queries))))
             self._run_layers(main)
         finally:
             # every fork is joined, also when a call raised
