@@ -154,6 +154,37 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
   const int row = (threadIdx.x & 63) >> 4;
   return x + (row == 0 ? 0u : (row == 1 ? t0 : (row == 2 ? t1 : t2)));
 }
+// Across the workgroup's waves: c[w][s] holds wave w's value (W <= 16 waves,
+// written before a barrier).  Lane w of the reading wave loads wave w's
+// value, so the first 16-lane row holds them all and a few DPP steps combine
+// them; the results are wave-uniform.  (Each lane summing all W values
+// itself took 2 W VALU instructions and a held lane mask per wave.)
+template <int W>
+__device__ __forceinline__ void wave_sums(const uint32_t (&c)[kTopkMaxWaves][2], int s, int wave,
+                                          uint32_t* before, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = lane < W ? c[lane][s] : 0u;
+  x += dpp_shr<0x111>(x);   // inclusive scan over the row
+  x += dpp_shr<0x112>(x);
+  x += dpp_shr<0x114>(x);
+  x += dpp_shr<0x118>(x);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)x, W - 1);
+  *before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)x, wave - 1) : 0u;
+}
+template <int W, class Op>
+__device__ __forceinline__ uint32_t wave_combine(const uint32_t (&c)[kTopkMaxWaves][2], int s, uint32_t ident,
+                                                 Op op) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = lane < W ? c[lane][s] : ident;
+  x = op(x, dpp_u<0xB1>(x));
+  x = op(x, dpp_u<0x4E>(x));
+  x = op(x, dpp_u<0x141>(x));
+  x = op(x, dpp_u<0x140>(x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+}
+__device__ __forceinline__ uint32_t min_u(uint32_t a, uint32_t b) { return min(a, b); }
+__device__ __forceinline__ uint32_t max_u(uint32_t a, uint32_t b) { return max(a, b); }
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -215,7 +246,7 @@ template <int THREADS, class Sh>
 __device__ __forceinline__ int find_bin(Sh& sh, uint32_t rem, uint32_t* above_out, uint32_t* count_out) {
   constexpr int W = THREADS / 64;
   constexpr int BPT = kBins / THREADS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t cb[BPT];
   uint32_t csum = 0u;
 #pragma unroll
@@ -226,9 +257,8 @@ __device__ __forceinline__ int find_bin(Sh& sh, uint32_t rem, uint32_t* above_ou
   const uint32_t x = wave_incl_scan(csum);
   if (lane == 63) sh.wcnt[wave][0] = x;
   __syncthreads();
-  uint32_t before = 0u;
-#pragma unroll
-  for (int w = 0; w < W; ++w) before += w < wave ? sh.wcnt[w][0] : 0u;
+  uint32_t before, total;
+  wave_sums<W>(sh.wcnt, 0, wave, &before, &total);
   const uint32_t above = before + x - csum;
   if (above < rem && rem <= above + csum) {
     uint32_t acc = above;
@@ -258,7 +288,7 @@ __device__ __forceinline__ void find_bin2(Sh& sh, uint32_t rem1, uint32_t rem2, 
                                           uint32_t* above1, uint32_t* b2, uint32_t* above2) {
   constexpr int W = THREADS / 64;
   constexpr int BPT = kBins / THREADS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t cb[BPT];
   uint32_t csum = 0u;
 #pragma unroll
@@ -270,9 +300,8 @@ __device__ __forceinline__ void find_bin2(Sh& sh, uint32_t rem1, uint32_t rem2, 
   const uint32_t x = wave_incl_scan(csum);
   if (lane == 63) sh.wcnt[wave][0] = x;
   __syncthreads();
-  uint32_t before = 0u;
-#pragma unroll
-  for (int w = 0; w < W; ++w) before += w < wave ? sh.wcnt[w][0] : 0u;
+  uint32_t before, total;
+  wave_sums<W>(sh.wcnt, 0, wave, &before, &total);
   const uint32_t above = before + x - csum;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -314,7 +343,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int n;
   if (MODE == MODE_KEYS) {
     const int L = a.len[row];
@@ -448,9 +477,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
     const uint32_t x = wave_incl_scan(cnt);
     if (lane == 63) sh.wcnt[wave][1] = x;
     __syncthreads();
-    uint32_t before = 0u;
-#pragma unroll
-    for (int w = 0; w < W; ++w) before += w < wave ? sh.wcnt[w][1] : 0u;
+    uint32_t before, total;
+    wave_sums<W>(sh.wcnt, 1, wave, &before, &total);
     const uint32_t excl = before + x - cnt;
     uint32_t gpre = excl >> 16, qpre = excl & 0xffffu;
     for (uint32_t i = s0; i < s1; ++i) {
@@ -602,15 +630,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
     }
     for (int b = tid; b < kBins; b += THREADS) sh.hist[b] = 0u;
     __syncthreads();
-    szmin = 0xffffffffu;
-    symax = 0u;
-    kall = 0u;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      szmin = min(szmin, sh.wred[w][0]);
-      symax = max(symax, sh.wred[w][1]);
-      kall = max(kall, sh.wcnt[w][1]);
-    }
+    szmin = wave_combine<W>(sh.wred, 0, 0xffffffffu, min_u);
+    symax = wave_combine<W>(sh.wred, 1, 0u, max_u);
+    kall = wave_combine<W>(sh.wcnt, 1, 0u, max_u);
     uint32_t smin = 0x80000000u, smax = 0x80000000u;
     if (szmin <= 0xfefffffeu) {
       smin = szmin + 0x00800001u;
@@ -641,14 +663,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       for (int e = 0; e < 4; ++e) wn += (uint32_t)__popcll(__ballot(key[j][e] >= theta));
     if (lane == 0) sh.wcnt[wave][0] = wn;
     __syncthreads();
-    uint32_t p = 0u, tot = 0u;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const uint32_t v = sh.wcnt[w][0];
-      p += w < wave ? v : 0u;
-      tot += v;
-    }
-    tot = __builtin_amdgcn_readfirstlane(tot);
+    uint32_t p, tot;
+    wave_sums<W>(sh.wcnt, 0, wave, &p, &tot);
     if (sbin != 0u && tot >= (uint32_t)k && tot <= (uint32_t)kList) {   // uniform
       write_list(0, theta, p);
       __syncthreads();
@@ -688,13 +704,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
   }
   if (tid == 0) sh.bcast[2] = 0u;   // register path: candidate list length
   __syncthreads();
-  zmin = 0xffffffffu;
-  ymax = 0u;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    zmin = min(zmin, sh.wred[w][0]);
-    ymax = max(ymax, sh.wred[w][1]);
-  }
+  zmin = wave_combine<W>(sh.wred, 0, 0xffffffffu, min_u);
+  ymax = wave_combine<W>(sh.wred, 1, 0u, max_u);
   uint32_t kmin = 0x80000000u, kmax = 0x80000000u;   // no finite key: any finite stand-in
   if (zmin <= 0xfefffffeu) {
     kmin = zmin + 0x00800001u;
@@ -756,13 +767,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
         for (int e = 0; e < 4; ++e) wn += (uint32_t)__popcll(__ballot(key[j][e] >= floor_key));
       if (lane == 0) sh.wcnt[wave][0] = wn;
       __syncthreads();
-      uint32_t p = m, tot = 0u;
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const uint32_t v = sh.wcnt[w][0];
-        p += w < wave ? v : 0u;
-        tot += v;
-      }
+      uint32_t p, tot;
+      wave_sums<W>(sh.wcnt, 0, wave, &p, &tot);
+      p += m;
       write_list(c, floor_key, p);
       m += tot;
       __syncthreads();
@@ -874,17 +881,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       sh.wcnt[wave][1] = eq;
     }
     __syncthreads();
-    uint32_t gbefore = gt_run, ebefore = eq_run, gtot = 0u, etot = 0u;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const uint32_t g = sh.wcnt[w][0], q = sh.wcnt[w][1];
-      if (w < wave) {
-        gbefore += g;
-        ebefore += q;
-      }
-      gtot += g;
-      etot += q;
-    }
+    uint32_t gbefore, ebefore, gtot, etot;
+    wave_sums<W>(sh.wcnt, 0, wave, &gbefore, &gtot);
+    wave_sums<W>(sh.wcnt, 1, wave, &ebefore, &etot);
+    gbefore += gt_run;
+    ebefore += eq_run;
     // an opaque copy of K keeps the counting ballots above from being reused
     // (and all held live) here
     uint32_t Kc = __builtin_amdgcn_readfirstlane(K);
