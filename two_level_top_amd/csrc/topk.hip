@@ -285,7 +285,8 @@ __device__ __forceinline__ int find_bin(Sh& sh, uint32_t rem, uint32_t* above_ou
 // < 2^16), one scan.
 template <int THREADS, class Sh>
 __device__ __forceinline__ void find_bin2(Sh& sh, uint32_t rem1, uint32_t rem2, uint32_t* b1,
-                                          uint32_t* above1, uint32_t* b2, uint32_t* above2) {
+                                          uint32_t* above1, uint32_t* count1, uint32_t* b2,
+                                          uint32_t* above2, uint32_t* count2) {
   constexpr int W = THREADS / 64;
   constexpr int BPT = kBins / THREADS;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -316,6 +317,7 @@ __device__ __forceinline__ void find_bin2(Sh& sh, uint32_t rem1, uint32_t rem2, 
         if (acc < rem && rem <= acc + v) {
           sh.bcast[4 * h] = (uint32_t)(kBins - 1 - BPT * tid - q);
           sh.bcast[4 * h + 1] = acc;
+          sh.bcast[4 * h + 2] = v;
         }
         acc += v;
       }
@@ -324,8 +326,10 @@ __device__ __forceinline__ void find_bin2(Sh& sh, uint32_t rem1, uint32_t rem2, 
   __syncthreads();
   *b1 = sh.bcast[0];
   *above1 = sh.bcast[1];
+  *count1 = sh.bcast[2];
   *b2 = sh.bcast[4];
   *above2 = sh.bcast[5];
+  *count2 = sh.bcast[6];
   __syncthreads();
 }
 
@@ -431,7 +435,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
 
   // write (index, key) of chunk c's elements >= F to the LDS list in index
   // order, from slot p of this wave on (p: the elements >= F before this
-  // wave's slice); entries past the list's capacity are dropped
+  // wave's slice).  Both callers have counted the row's elements >= F (or an
+  // upper bound of them) to at most the list's capacity first, so every slot
+  // is inside the list.
   auto write_list = [&](int c, uint32_t F0, uint32_t p) {
     // an opaque copy of the bound keeps the counting ballots of the caller
     // from being reused (and all held live) here
@@ -450,8 +456,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (key[j][e] >= F) {
-            if (q < (uint32_t)kList)
-              *reinterpret_cast<uint2*>(&sh.list[2 * q]) = make_uint2((uint32_t)(ib + e), key[j][e]);
+            *reinterpret_cast<uint2*>(&sh.list[2 * q]) = make_uint2((uint32_t)(ib + e), key[j][e]);
             ++q;
           }
         }
@@ -515,6 +520,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       need -= ab;
       fixed |= d << sh_lo;
       low = sh_lo;
+      if (cnt == need) {
+        // every entry of the bin is kept: the selection is the entries at or
+        // above the bin's lower edge (ties inside it are all taken, so the
+        // tie rule has nothing to decide), and the low bits need no pass
+        ordered_output(base + fixed - 1u, 0u, m, out, n_kept, kk);
+        return;
+      }
       // (score rows only: in the gathered and nested block selects the extra
       // code cost more registers than the saved pass gained)
       if (kRankFinish && low > 0 && cnt <= 64u) {
@@ -554,7 +566,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
   // same passes, one histogram each, then written one after the other.
   auto refine_dual = [&](uint32_t base, int low, uint32_t m) {
     uint32_t need1 = (uint32_t)a.k, need2 = (uint32_t)a.k2, fixed1 = 0u, fixed2 = 0u;
-    while (low > 0) {
+    // a selection whose bin is kept whole is done (as in refine_output): its
+    // threshold is the bin's lower edge, and it takes no more passes
+    bool done1 = false, done2 = false;
+    while (low > 0 && !(done1 && done2)) {
       const int width = low < 11 ? low : 11;
       const int sh_lo = low - width;
       const uint32_t hi_mask = low >= 32 ? 0u : ~((1u << low) - 1u);
@@ -567,21 +582,29 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDE
       for (uint32_t i = tid; i < m; i += THREADS) {
         const uint32_t r = sh.list[2 * i + 1] - base;
         const uint32_t hi = r & hi_mask, d = (r >> sh_lo) & msk;
-        if (hi == fixed1) atomicAdd(&sh.hist[d], 1u);
-        if (hi == fixed2) atomicAdd(&sh.hist2[d], 1u);
+        if (!done1 && hi == fixed1) atomicAdd(&sh.hist[d], 1u);
+        if (!done2 && hi == fixed2) atomicAdd(&sh.hist2[d], 1u);
       }
       __syncthreads();
-      uint32_t d1, ab1, d2, ab2;
-      find_bin2<THREADS>(sh, need1, need2, &d1, &ab1, &d2, &ab2);
-      need1 -= ab1;
-      need2 -= ab2;
-      fixed1 |= d1 << sh_lo;
-      fixed2 |= d2 << sh_lo;
+      uint32_t d1, ab1, c1, d2, ab2, c2;
+      find_bin2<THREADS>(sh, need1, need2, &d1, &ab1, &c1, &d2, &ab2, &c2);
+      if (!done1) {
+        need1 -= ab1;
+        fixed1 |= d1 << sh_lo;
+        done1 = c1 == need1;
+      }
+      if (!done2) {
+        need2 -= ab2;
+        fixed2 |= d2 << sh_lo;
+        done2 = c2 == need2;
+      }
       low = sh_lo;
     }
-    ordered_output(base + fixed1, need1, m, a.out + (int64_t)row * a.k, a.n_kept, a.k);
+    ordered_output(done1 ? base + fixed1 - 1u : base + fixed1, done1 ? 0u : need1, m,
+                   a.out + (int64_t)row * a.k, a.n_kept, a.k);
     __syncthreads();   // the first output has read the list counts
-    ordered_output(base + fixed2, need2, m, a.out2 + (int64_t)row * a.k2, a.n_kept2, a.k2);
+    ordered_output(done2 ? base + fixed2 - 1u : base + fixed2, done2 ? 0u : need2, m,
+                   a.out2 + (int64_t)row * a.k2, a.n_kept2, a.k2);
   };
 
   // the k2 best blocks from the list of a first selection: every entry is at
