@@ -336,8 +336,20 @@ __device__ __forceinline__ void find_bin2(Sh& sh, uint32_t rem1, uint32_t rem2, 
 // RESIDENT: every row fits one chunk (n <= THREADS * 32), loaded once.
 // NEST (block keys only): also the nested k2 best blocks (a kernel of its own,
 // so that the plain block selection carries none of it)
+// Waves per SIMD: a resident 1024-thread row needs 8 for two rows per CU; the
+// 512-thread score-row selects too (four rows per CU at 64 VGPRs, a few
+// spilled: consumer top-512 0.335 -> 0.303 ms on the long chunk), the others
+// keep 6 (their extra code would spill more).
+template <int MODE, int THREADS, bool RESIDENT>
+constexpr int topk_waves_per_eu() {
+  if (!RESIDENT) return 4;
+  if (THREADS == 1024) return 8;
+  if (THREADS == 512) return (MODE == MODE_BLOCKMAP || MODE == MODE_IDENTITY) ? 8 : 6;
+  return 4;
+}
+
 template <int MODE, bool VEC, int THREADS, bool RESIDENT, bool BF16, bool NEST = false>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(!RESIDENT ? 4 : THREADS == 1024 ? 8 : THREADS == 512 ? 6 : 4))) void topk_kernel(TopkArgs a) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_waves_per_eu<MODE, THREADS, RESIDENT>()))) void topk_kernel(TopkArgs a) {
   constexpr int W = THREADS / 64;
   constexpr int kChunk = W * kWaveSlice;
   constexpr bool kMapped = MODE == MODE_BLOCKMAP || MODE == MODE_GATHER;
