@@ -5,8 +5,8 @@
 // each row's [ks, ke)).
 //
 // Work decomposition (gfx950: 256 CUs in 8 XCDs, wave64):
-//   workgroup = 4 waves, 8 query rows (2 per wave), 1024 positions (512 or
-//   256 when there are too few rows to fill the chip otherwise, as in decode).
+//   workgroup = 4 waves, 8 query rows (2 per wave), 4096 positions (halved,
+//   down to 256, while fewer than 2048 workgroups would run, as in decode).
 //   workgroup id -> (row group = id / nchunks, chunk = id % nchunks), so
 //   consecutive ids -- which the dispatcher spreads over the 8 XCDs -- share
 //   a row group and walk different position chunks: each XCD keeps 1/8 of
@@ -41,9 +41,11 @@
 
 namespace idxk {
 
-// positions per workgroup: 1024, or 512 / 256 when there are few rows (decode)
-// so that at least kDenseTargetWGs workgroups run
-constexpr int kDenseMaxChunk = 1024;
+// positions per workgroup: 4096, halved while fewer than kDenseTargetWGs
+// workgroups would run (decode).  Longer chunks spread a wave's query loads
+// and setup over more tiles: 4096 against 1024 took the long chunk's dense
+// pass from 19.37-19.56 to 19.30-19.34 ms.
+constexpr int kDenseMaxChunk = 4096;
 constexpr int kDenseMinChunk = 256;
 constexpr int64_t kDenseTargetWGs = 2048;
 constexpr int kDenseWaves = 4;
@@ -100,7 +102,7 @@ __device__ __forceinline__ int page_tile_scale(const PageOps& o, int t, int sdis
 }
 
 // Score NR (1 or 2) rows of one request against positions [c0, cend) (c0 on
-// a page boundary, at most 16 pages).  Every tile of a page is computed;
+// a page boundary, at most 64 pages: their ids sit one per lane).  Every tile of a page is computed;
 // positions past a row's length are never stored.  With keys, Krow[r] gets
 // the keys of blocks [c0/8, min(cend/8, nblk[r])) (Krow[r] is only used when
 // nblk[r] > 0, i.e. the row is keyed).
