@@ -110,6 +110,27 @@ __device__ __forceinline__ uint32_t value_key(uint32_t u) {
   return (u ^ s) + c;
 }
 
+// Raw fp32 bit patterns of a resident row on the sampled path (see the
+// kernel): an empty slot holds a quiet NaN, which every float compare puts
+// below any bound and the max below ignores.
+constexpr uint32_t kRawEmpty = 0x7fc00000u;
+// key of a raw pattern; NaN (an empty slot) -> 0, the empty key
+__device__ __forceinline__ uint32_t raw_key(uint32_t u) {
+  return (u & 0x7fffffffu) > 0x7f800000u ? 0u : value_key(u);
+}
+// the fp32 value whose key is `key` (keys of finite values and +-inf; +0 for
+// the shared key of +0 and -0), for comparing raw patterns against a key bound
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __uint_as_float(key >= 0x80000000u ? key - 0x80000000u : 0u - key);
+}
+// max of three fp32 patterns, NaN operands ignored (IEEE mode); written out
+// because the compiler would canonicalize every operand of fmaxf first
+__device__ __forceinline__ uint32_t fmax3_bits(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // Wave-wide reductions and scans on DPP and permlane moves (VALU only; the
 // shuffle forms go through LDS with a round trip per step).
 template <int CTRL>
@@ -402,6 +423,11 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
   int32_t* const n_kept = second ? a.n_kept2 : a.n_kept;
 
   const int nchunks = RESIDENT ? 1 : (n + kChunk - 1) / kChunk;
+  // A resident row that tries the sampled bound is held as raw fp32 patterns
+  // (kRawEmpty in empty slots) and compared as floats, which saves the three
+  // key instructions per element; only the sample, the list entries and a
+  // row that falls back to the full path are turned into keys.
+  constexpr bool kRaw = RESIDENT && kSampledBound && MODE != MODE_GATHER;
   uint32_t key[kTopkSteps][4];
   // element index of key[j][e] in chunk c: c * kChunk + ebase + 256 j + e
   const int ebase = wave * kWaveSlice + 4 * lane;
@@ -414,7 +440,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
         bool ok[4];
         load4<MODE, VEC, BF16, false>(a, Xr, blk, i, n, u, ok);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[j][e] = value_key(u[e]);
+        for (int e = 0; e < 4; ++e) key[j][e] = kRaw ? u[e] : value_key(u[e]);
       }
     } else {
       // the row ends in this chunk: only the wave's step that straddles the
@@ -431,14 +457,14 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
         if (MODE != MODE_GATHER && s0 + 256 <= n) {
           load4<MODE, VEC, BF16, false>(a, Xr, blk, i, n, u, ok);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) key[j][e] = value_key(u[e]);
+          for (int e = 0; e < 4; ++e) key[j][e] = kRaw ? u[e] : value_key(u[e]);
         } else if (MODE != MODE_GATHER && s0 >= n) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) key[j][e] = 0u;
+          for (int e = 0; e < 4; ++e) key[j][e] = kRaw ? kRawEmpty : 0u;
         } else {
           load4<MODE, VEC, BF16, true>(a, Xr, blk, i, n, u, ok);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) key[j][e] = ok[e] ? value_key(u[e]) : 0u;
+          for (int e = 0; e < 4; ++e) key[j][e] = ok[e] ? (kRaw ? u[e] : value_key(u[e])) : (kRaw ? kRawEmpty : 0u);
         }
       }
     }
@@ -468,6 +494,34 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (key[j][e] >= F) {
+            *reinterpret_cast<uint2*>(&sh.list[2 * q]) = make_uint2((uint32_t)(ib + e), key[j][e]);
+            ++q;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p += (uint32_t)__popcll(G[e]);
+      }
+    }
+  };
+
+  // write_list on raw patterns (the sampled path): elements whose value is at
+  // or above the bound key F0's value, written as raw patterns (keyed after)
+  auto write_list_raw = [&](uint32_t F0, uint32_t p) {
+    float F = key_float(__builtin_amdgcn_readfirstlane(F0));
+    asm volatile("" : "+s"(F));
+#pragma unroll
+    for (int j = 0; j < kTopkSteps; ++j) {
+      uint64_t G[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) G[e] = __ballot(__uint_as_float(key[j][e]) >= F);
+      if ((G[0] | G[1] | G[2] | G[3]) != 0u) {
+        uint32_t q = p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q += lanes_below(G[e]);
+        const int ib = ebase + 256 * j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (__uint_as_float(key[j][e]) >= F) {
             *reinterpret_cast<uint2*>(&sh.list[2 * q]) = make_uint2((uint32_t)(ib + e), key[j][e]);
             ++q;
           }
@@ -646,15 +700,15 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
   // 0.39 -> 0.36 ms.  The gathered mode, bound by its scattered loads, ran
   // 25% slower with it, whatever the sample positions, so it keeps the full
   // path.)
-  if (RESIDENT && kSampledBound && MODE != MODE_GATHER) {
-    const uint32_t sa = key[0][0], sb = key[kTopkSteps / 2][2];
+  if (kRaw) {
+    const uint32_t sa = raw_key(key[0][0]), sb = raw_key(key[kTopkSteps / 2][2]);
     uint32_t symax = max(sa + 0x00800000u, sb + 0x00800000u);
     uint32_t szmin = min(sa - 0x00800001u, sb - 0x00800001u);
-    uint32_t kall = 0u;   // the row's largest key (+inf included): the refine width
+    // the row's largest key (+inf included): the refine width
+    uint32_t vmax = kRawEmpty;
 #pragma unroll
-    for (int j = 0; j < kTopkSteps; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kall = max(kall, key[j][e]);
+    for (int j = 0; j < kTopkSteps; ++j) vmax = fmax3_bits(fmax3_bits(vmax, key[j][0], key[j][1]), key[j][2], key[j][3]);
+    uint32_t kall = raw_key(vmax);
     symax = wave_max(symax);
     szmin = wave_min(szmin);
     kall = wave_max(kall);
@@ -691,17 +745,22 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
     uint32_t sab, scnt;
     const uint32_t sbin = (uint32_t)find_bin<THREADS>(sh, r, &sab, &scnt);
     const uint32_t theta = sbin == 0u ? kPosInf : (sbin >= sinf ? kPosInf : slo + (sbin << sshift));
+    // (theta >= the sample's smallest finite key, so it is the key of a value:
+    // a float compare with that value counts the elements whose key is >= theta)
+    const float thf = key_float(theta);
     uint32_t wn = 0u;
 #pragma unroll
     for (int j = 0; j < kTopkSteps; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wn += (uint32_t)__popcll(__ballot(key[j][e] >= theta));
+      for (int e = 0; e < 4; ++e) wn += (uint32_t)__popcll(__ballot(__uint_as_float(key[j][e]) >= thf));
     if (lane == 0) sh.wcnt[wave][0] = wn;
     __syncthreads();
     uint32_t p, tot;
     wave_sums<W>(sh.wcnt, 0, wave, &p, &tot);
     if (sbin != 0u && tot >= (uint32_t)k && tot <= (uint32_t)kList) {   // uniform
-      write_list(0, theta, p);
+      write_list_raw(theta, p);
+      __syncthreads();
+      for (uint32_t i = tid; i < tot; i += THREADS) sh.list[2 * i + 1] = value_key(sh.list[2 * i + 1]);
       __syncthreads();
       const uint32_t span = kall - theta;
       if constexpr (NEST) {
@@ -715,6 +774,13 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
     }
   }
 
+
+  if (kRaw) {   // the sample gave no bound: the row's keys, in place
+#pragma unroll
+    for (int j = 0; j < kTopkSteps; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[j][e] = raw_key(key[j][e]);
+  }
 
   // ---- 1a. finite extremes of the row ----
   // y = key + 2^23 sends +inf to 0 (below every finite key); z = key - 2^23 - 1
