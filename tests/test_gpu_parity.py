@@ -452,7 +452,7 @@ def test_topk_rows_bf16_bitexact(idx, kb, k):
 # when that overflows too: the cluster sizes below reach each of these, with
 # and without exact ties at the threshold, in one chunk and across chunks.
 CROWDS = [("constant", 0), ("zeros", 0), ("cluster", 3000), ("cluster", 8000), ("neginf", 0),
-          ("posinf", 0), ("posinf_many", 0)]
+          ("posinf", 0), ("posinf_many", 0), ("subnormal", 0)]
 
 
 @pytest.mark.parametrize("width,k", [(16384, 512), (32768, 2048), (1024, 32), (70000, 512)])

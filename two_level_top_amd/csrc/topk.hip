@@ -30,7 +30,11 @@
 //      sample of two keys per thread to pick a bound that between k and the
 //      list's capacity elements reach, checked by one counting pass; then
 //      step 2 runs at once and step 3 finds K on the list from the top bit
-//      down.  A row whose sample does not give such a bound takes steps 1-3.
+//      down.  On this path the registers hold the raw fp32 patterns and are
+//      compared as floats with the value of the bound key (no per-element key
+//      instructions); the list entries are keyed after the list pass.  A row
+//      whose sample does not give such a bound keys its registers in place
+//      and takes steps 1-3.
 //   1. threshold bin: one histogram pass over the digit
 //      1 + ((key - kmin) >> shift), kmin/kmax being the finite extremes of the
 //      row and shift the smallest one that fits the span in 2046 bins (-inf
@@ -739,9 +743,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(topk_wa
     atomicAdd(&sh.hist[min(__builtin_elementwise_sub_sat(sa, slo), stop) >> sshift], 1u);
     atomicAdd(&sh.hist[min(__builtin_elementwise_sub_sat(sb, slo), stop) >> sshift], 1u);
     __syncthreads();
-    // r = k/16 plus three standard deviations of the sample's count
+    // r = k/16 plus three standard deviations of the sample's count (a margin:
+    // the bare v_sqrt_f32 serves, not the correctly rounded sqrtf sequence)
     const float kq = (float)k * (1.0f / 16.0f);
-    const uint32_t r = min((uint32_t)(2 * THREADS), (uint32_t)(kq + 3.0f * __builtin_sqrtf(kq)) + 1u);
+    const uint32_t r = min((uint32_t)(2 * THREADS), (uint32_t)(kq + 3.0f * __builtin_amdgcn_sqrtf(kq)) + 1u);
     uint32_t sab, scnt;
     const uint32_t sbin = (uint32_t)find_bin<THREADS>(sh, r, &sab, &scnt);
     const uint32_t theta = sbin == 0u ? kPosInf : (sbin >= sinf ? kPosInf : slo + (sbin << sshift));

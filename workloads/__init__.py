@@ -346,7 +346,10 @@ def crowded_rows(seed: int, kind: str, rows: int, width: int, k: int, cluster: i
                   two values at +1e30 and two at -1e30 widening the row's span;
       'neginf'    k // 2 finite values ~ N(0, 8^2), the rest -inf;
       'posinf'    k + k // 2 values +inf, the rest ~ N(0, 8^2);
-      'posinf_many'  a quarter of the row +inf, the rest ~ N(0, 8^2)."""
+      'posinf_many'  a quarter of the row +inf, the rest ~ N(0, 8^2);
+      'subnormal' multiples -300..300 of the smallest subnormal 2^-149
+                  (zeros of both signs among them), so the threshold and
+                  its neighbours are subnormal."""
     r = _rng(902, seed)
     x = np.empty((rows, width), np.float32)
     for i in range(rows):
@@ -364,6 +367,10 @@ def crowded_rows(seed: int, kind: str, rows: int, width: int, k: int, cluster: i
             v = np.full(width, -np.inf, np.float32)
             nf = min(k // 2, width)
             v[:nf] = r.standard_normal(nf) * 8.0
+        elif kind == "subnormal":
+            m = r.integers(-300, 301, width)
+            v = (m.astype(np.float64) * 2.0 ** -149).astype(np.float32)
+            v[(m == 0) & (r.random(width) < 0.5)] = np.float32(-0.0)
         elif kind in ("posinf", "posinf_many"):
             v = (r.standard_normal(width) * 8.0).astype(np.float32)
             ni = min(width, k + k // 2 if kind == "posinf" else width // 4)
