@@ -235,6 +235,34 @@ def test_q_rope_quant_bitexact(idx, rows, heads, neox):
     assert np.array_equal(host(w_out[idx_t]).view(np.uint32), w_o.view(np.uint32)), "weights differ"
 
 
+def test_q_rope_quant_edge_values(idx):
+    """Exact ties of the e2m1 grid, zeros of both signs, negative values that
+    round to zero and values at the top of the grid, each group scaled by its
+    own power of two, at position 0 (the rotation is then the identity, so the
+    quantiser sees these values as they are)."""
+    from oracle import q_quant
+    rows, heads = 64, 64
+    rng = np.random.default_rng(5)
+    specials = np.array([0.0, -0.0, 0.25, -0.25, 0.75, -0.75, 1.25, -1.25, 1.75, -1.75, 2.5, -2.5,
+                         3.5, -3.5, 5.0, -5.0, 6.0, -6.0, 4.0, -3.0, 0.1, -0.1, 0.2, -0.2], np.float32)
+    x = rng.choice(specials, size=(rows, heads, 128)).astype(np.float32)
+    x *= np.exp2(rng.integers(-20, 21, size=(rows, heads, 4))).repeat(32, axis=-1).astype(np.float32)
+    bits, _ = workloads.to_bf16(x)
+    positions = np.zeros(rows, np.int32)
+    cos_sin = workloads.rope_table(4096)
+    w = rng.standard_normal((rows, heads)).astype(np.float32)
+    say("q rope quant edge values")
+    q = torch.from_numpy(bits.view(np.int16)).cuda()
+    vals = torch.full((rows, heads, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, heads, 4), 0xAB, dtype=torch.uint8, device="cuda")
+    w_out = torch.full((rows, heads), float("nan"), dtype=torch.float32, device="cuda")
+    for neox in (True, False):
+        idx.idx_q_rope_quant(q, dev(positions), dev(cos_sin), dev(w), neox, 1.0, 1.0, vals, scales, w_out)
+        v_o, s_o, _ = q_quant.q_rope_quant(bits, positions, cos_sin, w, neox, 1.0, 1.0)
+        assert np.array_equal(host(vals), v_o), "codes differ"
+        assert np.array_equal(host(scales), s_o), "scales differ"
+
+
 # ---------------------------------------------------------------------------
 # idx_score_dense_keys: the fused source pass
 # ---------------------------------------------------------------------------

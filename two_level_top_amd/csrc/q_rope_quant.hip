@@ -31,22 +31,25 @@ constexpr int kRqHeadsPerWG = 16 * kRqPerLane;   // heads per 256-thread workgro
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// nearest bf16 (ties to even), as fp32; finite inputs
-__device__ __forceinline__ float round_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  u = (u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u;
-  return __uint_as_float(u);
+// nearest bf16 (ties to even) of two fp32 values, as fp32: one
+// v_cvt_pk_bf16_f32 (which rounds finite values, subnormals and ties exactly
+// as (u + 0x7fff + ((u >> 16) & 1)) >> 16 does) and two unpacks
+__device__ __forceinline__ void round2_bf16(float& a, float& b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
+  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
+  a = __uint_as_float(lo << 16);
+  b = __uint_as_float(hi << 16);
 }
 
-__device__ __forceinline__ uint32_t e2m1_code(float a) {   // a >= 0
-  if (a <= 0.25f) return 0u;
-  if (a < 0.75f) return 1u;
-  if (a <= 1.25f) return 2u;
-  if (a < 1.75f) return 3u;
-  if (a <= 2.5f) return 4u;
-  if (a < 3.5f) return 5u;
-  if (a <= 5.0f) return 6u;
-  return 7u;
+// gfx950's v_cvt_scalef32_pk_fp4_f32 writes byte SEL of `old` with the e2m1
+// codes of a / scale (low nibble) and b / scale: nearest, ties to the even
+// code, saturated at 6 (checked against the rule above over a sweep of
+// values, ties, subnormals and values past 6 at several scales).  It writes
+// a negative value that rounds to zero as code 8 (-0); the caller maps those
+// to 0.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
 __device__ __forceinline__ float swizzle_xor4(float v) {
@@ -62,22 +65,35 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
 // quantise 8 values (dims 8j .. 8j+7) of one head; lanes of an aligned quad
 // share a 32-element group
 __device__ __forceinline__ void quantize8(const float (&x)[8], uint32_t& codes, int& e) {
-  uint32_t am = 0u;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) am = max(am, __float_as_uint(x[k]) & 0x7fffffffu);
+  // |x| maximum of the 8 values: v_max3_f32 with |.| source modifiers (finite
+  // inputs: the bit pattern of the largest magnitude), written out because
+  // the compiler would canonicalize every operand of fmaxf first
+  uint32_t am;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\t"
+      "v_max3_f32 %0, %0, |%4|, |%5|\n\t"
+      "v_max3_f32 %0, %0, |%6|, |%7|\n\t"
+      "v_max3_f32 %0, %0, |%8|, %0\n\t"
+      "s_nop 1"   // VALU write -> the DPP reads of am below
+      : "=&v"(am)
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
   am = max(am, dpp_u<0xB1>(am));   // quad_perm [1,0,3,2]
   am = max(am, dpp_u<0x4E>(am));   // quad_perm [2,3,0,1]
   const float raw_scale = fmaxf(__uint_as_float(am), 1e-10f) * (1.0f / 6.0f);
   const uint32_t rb = __float_as_uint(raw_scale);          // a positive normal value
   e = (int)((rb >> 23) & 0xffu) - 127 + ((rb & 0x7fffffu) != 0u ? 1 : 0);   // ceil(log2)
-  codes = 0u;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float y = ldexpf(x[k], -e);   // exact: power-of-two scale
-    uint32_t c = e2m1_code(fabsf(y));
-    if (y < 0.f && c != 0u) c |= 8u;
-    codes |= c << (4 * k);
-  }
+  // e lies in [-35, 126] (amax is at least 1e-10 and finite), so 2^e is a
+  // normal fp32 value and x / 2^e is exact
+  const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+  uint32_t w = 0u;
+  w = cvt_fp4x2<0>(w, x[0], x[1], scale);
+  w = cvt_fp4x2<1>(w, x[2], x[3], scale);
+  w = cvt_fp4x2<2>(w, x[4], x[5], scale);
+  w = cvt_fp4x2<3>(w, x[6], x[7], scale);
+  // -0 (code 8) -> code 0: keep a nibble's sign bit only where its magnitude
+  // is nonzero (magnitude + 7 carries into bit 3 exactly then; no nibble
+  // carries into the next)
+  const uint32_t mag = w & 0x77777777u;
+  codes = mag | (w & ((mag + 0x77777777u) & 0x88888888u));
 }
 
 // One workgroup per (row, 64 heads): 16 lanes per head, each 16-lane group
@@ -106,7 +122,10 @@ __global__ __launch_bounds__(256) void q_rope_quant_kernel(const uint16_t* __res
     const int h = min(h0 + 16 * t, heads - 1);   // past the last head: a copy, never stored
     raw[t] = *reinterpret_cast<const uint4*>(q + (rbase + h) * kDim + 8 * j);
   }
-  // this lane's angles: NeoX pairs i = 8 (j % 4) + k, interleaved i = 4j + m
+  // this lane's angles: NeoX pairs i = 8 (j % 4) + k, interleaved i = 4j + m.
+  // In the NeoX layout lane j < 4 computes r0 = x0 cos - x1 sin as
+  // x0 cos + x1 (-sin) (the same rounded products and sum), so that both
+  // halves of the pair run one code path.
   float c[8], s[8];
   if (j < 8) {
     const int i0 = NEOX ? 8 * (j & 3) : 4 * j;
@@ -119,6 +138,10 @@ __global__ __launch_bounds__(256) void q_rope_quant_kernel(const uint16_t* __res
       const float4 s1 = *reinterpret_cast<const float4*>(cs + 32 + i0 + 4);
       c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
       s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
+      if (j < 4) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s[k] = -s[k];
+      }
     }
   }
 #pragma unroll
@@ -136,20 +159,20 @@ __global__ __launch_bounds__(256) void q_rope_quant_kernel(const uint16_t* __res
       float other[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) other[k] = swizzle_xor4(x[k]);
-      if (j < 4) {
+      if (j < 8) {   // r0 (j < 4, sines negated above) or r1
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = round_bf16(x[k] * c[k] - other[k] * s[k]);   // r0
-      } else if (j < 8) {
+        for (int k = 0; k < 8; ++k) x[k] = x[k] * c[k] + other[k] * s[k];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = round_bf16(x[k] * c[k] + other[k] * s[k]);   // r1
+        for (int k = 0; k < 8; k += 2) round2_bf16(x[k], x[k + 1]);
       }
     } else if (j < 8) {
       // pairs (2i, 2i + 1): lane j holds i = 4j .. 4j+3
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float x0 = x[2 * m], x1 = x[2 * m + 1];
-        x[2 * m] = round_bf16(x0 * c[m] - x1 * s[m]);
-        x[2 * m + 1] = round_bf16(x1 * c[m] + x0 * s[m]);
+        x[2 * m] = x0 * c[m] - x1 * s[m];
+        x[2 * m + 1] = x1 * c[m] + x0 * s[m];
+        round2_bf16(x[2 * m], x[2 * m + 1]);
       }
     }
     uint32_t codes;
