@@ -19,35 +19,62 @@
 
 namespace idxk {
 
+// One workgroup per (row, 256 * VEC candidates): thread t expands candidates
+// VEC t .. VEC t + VEC - 1 of its slice (VEC = 4: one 16-byte load of block
+// ids and one 16-byte store, when kb % 4 == 0 and both arrays are 16-byte
+// aligned).  The row's first workgroup also writes the row's work-list
+// entries (and row 0's the entry count), so the list needs no launch of its
+// own.
+template <int VEC>
 __global__ __launch_bounds__(256) void expand_kernel(PoolArgs kp, const int32_t* __restrict__ req,
-                                                     const int32_t* __restrict__ len, int kb,
+                                                     const int32_t* __restrict__ len, int rows, int kb,
                                                      const int32_t* __restrict__ blocks,
                                                      const int32_t* __restrict__ n_kept,
                                                      int32_t* __restrict__ phys,
                                                      int32_t* __restrict__ valid_len,
                                                      int32_t* __restrict__ len_out,
-                                                     int32_t* __restrict__ req_out, int chunks) {
+                                                     int32_t* __restrict__ req_out,
+                                                     int32_t* __restrict__ sched, int chunks) {
   const int row = blockIdx.x / chunks;
-  const int i = (blockIdx.x % chunks) * 256 + threadIdx.x;
+  const int chunk = blockIdx.x % chunks;
+  const int i0 = (chunk * 256 + (int)threadIdx.x) * VEC;
   const int nk = min(max(n_kept[row], 0), kb);
   const int rq = req[row];
   const int rqc = clamp_req(rq, kp.num_req);
-  if (i < kb) {
-    int32_t v = -1;
-    if (i < nk) {
-      const int b = blocks[(int64_t)row * kb + i];
-      const int pi = min(max(b / kBlocksPerPage, 0), kp.max_pages - 1);
-      const int32_t page = kp.page_table[(int64_t)rqc * kp.max_pages + pi];
-      v = page * kBlocksPerPage + b % kBlocksPerPage;
+  const int32_t* pt = kp.page_table + (int64_t)rqc * kp.max_pages;
+  auto slot = [&](int b) {
+    const int pi = min(max(b / kBlocksPerPage, 0), kp.max_pages - 1);
+    return pt[pi] * kBlocksPerPage + b % kBlocksPerPage;
+  };
+  if (i0 < kb) {
+    const int64_t base = (int64_t)row * kb + i0;
+    if (VEC == 4) {
+      const int4 b = *reinterpret_cast<const int4*>(blocks + base);
+      int4 v;
+      v.x = i0 < nk ? slot(b.x) : -1;
+      v.y = i0 + 1 < nk ? slot(b.y) : -1;
+      v.z = i0 + 2 < nk ? slot(b.z) : -1;
+      v.w = i0 + 3 < nk ? slot(b.w) : -1;
+      *reinterpret_cast<int4*>(phys + base) = v;
+    } else {
+      phys[base] = i0 < nk ? slot(blocks[base]) : -1;
     }
-    phys[(int64_t)row * kb + i] = v;
   }
-  if (i == 0) {
-    const int L = len[row];
-    const int nblk = L > 0 ? (L + kBlock - 1) / kBlock : 0;
-    valid_len[row] = L > 0 ? kBlock * nk - (kBlock * nblk - L) : 0;
-    len_out[row] = L;
-    req_out[row] = rq;
+  if (chunk == 0) {
+    const int units = (kb + kUnitBlocks - 1) / kUnitBlocks;
+    for (int u = (int)threadIdx.x; u < units; u += 256) {
+      const int64_t e = (int64_t)row * units + u;
+      sched[4 + 2 * e] = row;
+      sched[5 + 2 * e] = u * kUnitBlocks < nk ? u * kUnitBlocks : -1;
+    }
+    if (threadIdx.x == 0) {
+      const int L = len[row];
+      const int nblk = L > 0 ? (L + kBlock - 1) / kBlock : 0;
+      valid_len[row] = L > 0 ? kBlock * nk - (kBlock * nblk - L) : 0;
+      len_out[row] = L;
+      req_out[row] = rq;
+      if (row == 0) sched[0] = rows * units;
+    }
   }
 }
 
@@ -172,14 +199,20 @@ hipError_t launch_expand(const PoolArgs& kp, const int32_t* req, const int32_t* 
                          int32_t* valid_len, int32_t* len_out, int32_t* req_out, void* schedule,
                          hipStream_t st) {
   if (rows <= 0) return launch_schedule(n_kept, 0, kb, schedule, st);
-  const int chunks = (kb + 255) / 256;
+  const bool vec = kb % 4 == 0 && reinterpret_cast<uintptr_t>(blocks) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(phys) % 16 == 0;
+  const int per_wg = vec ? 1024 : 256;
+  const int chunks = (kb + per_wg - 1) / per_wg;
   const int64_t grid = (int64_t)rows * chunks;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(expand_kernel, dim3((unsigned)grid), dim3(256), 0, st, kp, req, len, kb,
-                     blocks, n_kept, phys, valid_len, len_out, req_out, chunks);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_schedule(n_kept, rows, kb, schedule, st);
+  int32_t* sched = static_cast<int32_t*>(schedule);
+  if (vec)
+    hipLaunchKernelGGL(expand_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, kp, req, len, rows, kb,
+                       blocks, n_kept, phys, valid_len, len_out, req_out, sched, chunks);
+  else
+    hipLaunchKernelGGL(expand_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, kp, req, len, rows, kb,
+                       blocks, n_kept, phys, valid_len, len_out, req_out, sched, chunks);
+  return hipGetLastError();
 }
 
 size_t tail_workspace_bytes(int num_req) {
