@@ -5,8 +5,9 @@
 // order; no dense row is formed).
 //
 // The work list (built by idx_expand_candidates) holds one unit per 64
-// candidate blocks of a row.  A wave takes 8 consecutive units (the list is
-// row-major, so mostly of one row), keeps the row's query in registers across
+// candidate blocks of a row.  A wave takes a run of 4 consecutive units of
+// one row (runs ordered so that the waves running at one time hold the same
+// run of every row, see the kernel), keeps the row's query in registers across
 // them, loads each unit's 64 pool-block ids once (one per lane) and walks
 // 2 candidate blocks (16 positions) per MFMA tile, 4 tiles per group, two
 // groups in flight (ping-pong registers): lane l gathers 16 bytes of position
@@ -20,14 +21,16 @@ namespace idxk {
 
 constexpr int kSparseWaves = 4;
 // Work per wave, chosen at launch from the number of units so that about
-// kSparseTargetWaves waves run: up to 8 consecutive units per wave on big
-// tables (8 and 32 measured alike on MI355X, 1 was 8% slower: the query
-// reload and the wave launch per 512 columns), or a unit split over 2, 4 or
-// 8 waves (8 / split groups each) when there are fewer units than that.  On
-// 64 decode rows (2048 units) one unit per wave ran in 16 us against 26 us
-// split over 4 waves: each wave's query and block-id loads are fixed latency.
+// kSparseTargetWaves waves run: up to 4 consecutive units per wave on big
+// tables (one unit per wave was 8% slower: the query reload and the wave
+// launch per 512 columns; runs of 4, 8 and 16 units measured alike on the
+// consumer tables, 4 best on the 513-block source table and on prefill), or a
+// unit split over 2, 4 or 8 waves (8 / split groups each) when there are
+// fewer units than that.  On 64 decode rows (2048 units) one unit per wave
+// ran in 16 us against 26 us split over 4 waves: each wave's query and
+// block-id loads are fixed latency.
 constexpr int kSparseTargetWaves = 2048;
-constexpr int kMaxUnitsPerWave = 8;
+constexpr int kMaxUnitsPerWave = 4;
 // scores are stored non-temporally (cache policy nt): a consumer's 1 GB of
 // scores is read once, by its top-k, after the whole table is scored
 // (measured 2.13 -> 2.10 ms per call on the long chunk)
@@ -103,8 +106,23 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
   // row-major) and keeps the row's query in registers across them, or part
   // `part` of one unit when split > 1
   const int wid = blockIdx.x * kSparseWaves + wave;
-  const int u0 = split > 1 ? wid / split : wid * upw;
-  const int u1 = min(split > 1 ? u0 + 1 : u0 + upw, nunits);
+  int u0 = split > 1 ? wid / split : wid * upw;
+  int u1 = min(split > 1 ? u0 + 1 : u0 + upw, nunits);
+  if (split == 1 && upw > 1) {
+    // When a row's U units split evenly into runs of upw, wave wid takes run
+    // b = wid / rows of row wid % rows.  A row's candidates ascend through its
+    // context, so run b of every row covers about the same stretch of it;
+    // the waves running at one time then gather from the same pool pages
+    // (the rows of one request share them), which each XCD's L2 keeps:
+    // consumer scores 2.08 -> 2.00 ms on the long chunk, bit-identical.  The
+    // last workgroup's spare waves (b past the runs) take no unit.
+    const int U = (kb + kUnitBlocks - 1) / kUnitBlocks;
+    if (U % upw == 0) {
+      const int r = wid % q.rows, b = wid / q.rows;
+      u0 = b < U / upw ? r * U + b * upw : nunits;
+      u1 = min(u0 + upw, nunits);
+    }
+  }
   const int part = split > 1 ? wid % split : 0;
   const int gper = 8 / split;                      // groups per part
   int cur_row = -1;
