@@ -616,8 +616,8 @@ def _sparse_launch(rows, kb):
     """The consumer scorer's launch shape (score_sparse.hip): units per wave, or
     waves per unit, from the number of 64-block work units."""
     units = rows * ((kb + 63) // 64)
-    if units >= 2048 * 8:
-        return "upw", 8
+    if units >= 2048 * 4:
+        return "upw", 4
     if units >= 2048:
         return "upw", units // 2048
     split = 1
@@ -627,19 +627,23 @@ def _sparse_launch(rows, kb):
 
 
 # (rows, kb, context, heads): every launch shape of the consumer scorer --
-# split 8 / 4 / 2, one unit per wave, 2..8 units per wave, with a row's units
-# dividing evenly among waves (kb = 2048: 32 units) or waves spanning two rows
-# (kb = 64, 192, 320, and 7 units per wave over 32-unit rows)
+# split 8 / 4 / 2, one unit per wave, 2..4 units per wave, with a row's units
+# dividing evenly into runs (kb = 2048: 32 units; the runs are then ordered
+# run-major: run b of every row, then run b + 1) or waves spanning two rows
+# (kb = 64, 192, 320, and 3 units per wave over 32-unit rows)
 SPARSE_CASES = [
     (8, 1024, 9000, 64),      # split 8
     (16, 2048, 20000, 64),    # split 4
     (40, 2048, 20000, 24),    # split 2, three 16-head blocks
     (64, 2048, 20000, 8),     # one unit per wave, one 16-head block
-    (256, 2048, 20000, 64),   # 4 units per wave, a row's 32 units split evenly
-    (448, 2048, 20000, 64),   # 7 units per wave: waves span rows
+    (160, 2048, 20000, 64),   # runs of 2 units, run-major
+    (256, 2048, 20000, 64),   # runs of 4 units, run-major
+    (448, 2048, 20000, 64),   # runs of 4 units, run-major, 14 waves' rows per run
+    (200, 2048, 20000, 64),   # 3 units per wave: waves span rows
     (4096, 64, 2000, 64),     # 2 units per wave of 1 unit per row: two rows per wave
     (1000, 320, 4000, 64),    # 2 units per wave over 5-unit rows
-    (5462, 192, 3000, 64),    # 8 units per wave over 3-unit rows
+    (5462, 192, 3000, 64),    # 4 units per wave over 3-unit rows
+    (8193, 256, 3000, 64),    # one run of 4 units per row, run-major; the last workgroup's spare waves
 ]
 
 
