@@ -643,6 +643,7 @@ SPARSE_CASES = [
     (4096, 64, 2000, 64),     # 2 units per wave of 1 unit per row: two rows per wave
     (1000, 320, 4000, 64),    # 2 units per wave over 5-unit rows
     (5462, 192, 3000, 64),    # 4 units per wave over 3-unit rows
+    (1700, 320, 4000, 64),    # 4 units per wave over 5-unit rows: waves span rows
     (8193, 256, 3000, 64),    # one run of 4 units per row, run-major; the last workgroup's spare waves
 ]
 
