@@ -615,9 +615,11 @@ def test_expand_and_sparse_scores(idx, name):
 def _sparse_launch(rows, kb):
     """The consumer scorer's launch shape (score_sparse.hip): units per wave, or
     waves per unit, from the number of 64-block work units."""
-    units = rows * ((kb + 63) // 64)
+    U = (kb + 63) // 64
+    units = rows * U
     if units >= 2048 * 4:
-        return "upw", 4
+        # short rows not splitting into runs of 4 go whole when that still fills the GPU
+        return "upw", U if (U % 4 and U <= 12 and units >= 2048 * U) else 4
     if units >= 2048:
         return "upw", units // 2048
     split = 1
@@ -642,8 +644,9 @@ SPARSE_CASES = [
     (200, 2048, 20000, 64),   # 3 units per wave: waves span rows
     (4096, 64, 2000, 64),     # 2 units per wave of 1 unit per row: two rows per wave
     (1000, 320, 4000, 64),    # 2 units per wave over 5-unit rows
-    (5462, 192, 3000, 64),    # 4 units per wave over 3-unit rows
+    (5462, 192, 3000, 64),    # whole 3-unit rows, one per wave
     (1700, 320, 4000, 64),    # 4 units per wave over 5-unit rows: waves span rows
+    (640, 832, 8000, 64),     # 4 units per wave over 13-unit rows: waves span rows
     (8193, 256, 3000, 64),    # one run of 4 units per row, run-major; the last workgroup's spare waves
 ]
 
