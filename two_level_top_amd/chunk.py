@@ -46,8 +46,8 @@ consumer's sparse scores (two score buffers, the main stream waiting for the
 select that last read a buffer before rewriting it); the main stream waits
 for the select stream at the end.  On 64 decode rows this cut the step from
 0.326 to 0.298 ms; on 2048 and 16384 rows the sparse scores fill the GPU and
-moving the consumers' selects gains nothing (16384 rows: 34.43-34.58 ms
-against 34.30-34.44 ms), so there they stay on the main stream.
+moving the consumers' selects gains nothing (16384 rows: 27.90-28.05 ms
+against 27.66-27.90 ms), so there they stay on the main stream.
 
 Tail layers (prefill PR, "Tail rows"): the last `tail_layers` consumers
 score only the last tail_len[j] rows of each request j.  The side stream

@@ -175,17 +175,35 @@ __global__ __launch_bounds__(256) void score_sparse_kernel(QueryArgs q,
     const int g0 = part * gper;
     const int g1 = min(ngroups, g0 + gper);
     if (g0 >= g1) continue;
+    // Two groups in flight: each group's loads are issued before the previous
+    // group is computed.  Every load in the loop is unconditional (the last
+    // B load repeats group g1 - 1 when the count is odd): a load whose value
+    // is used only past a branch is moved there by the compiler, and an
+    // optional load makes the wait at the join cover it, both of which left
+    // half the groups' gathers exposed (long chunk: 1.98-2.02 -> 1.88-1.90 ms
+    // per consumer call, bit-identical).  The scheduling barriers keep the
+    // scheduler from pulling the next group's scale permutes into the
+    // current group's arithmetic, which would wait on that group's loads.
     GroupOps A, B;
     load_group(prs, bov, sov, sel_of(g0), ssel_of(g0), voff, soff, A);
-    for (int g = g0; g < g1; g += 2) {
-      const int gb = min(g + 1, g1 - 1);
-      load_group(prs, bov, sov, sel_of(gb), ssel_of(gb), voff, soff, B);
+    __builtin_amdgcn_sched_barrier(0);
+    const int gb0 = min(g0 + 1, g1 - 1);
+    load_group(prs, bov, sov, sel_of(gb0), ssel_of(gb0), voff, soff, B);
+    int g = g0;
+    for (; g + 2 < g1; g += 2) {
+      __builtin_amdgcn_sched_barrier(0);
       compute(g, A);
-      if (g + 1 >= g1) break;
-      const int ga = min(g + 2, g1 - 1);
-      load_group(prs, bov, sov, sel_of(ga), ssel_of(ga), voff, soff, A);
+      __builtin_amdgcn_sched_barrier(0);
+      load_group(prs, bov, sov, sel_of(g + 2), ssel_of(g + 2), voff, soff, A);
+      __builtin_amdgcn_sched_barrier(0);
       compute(g + 1, B);
+      __builtin_amdgcn_sched_barrier(0);
+      const int gb = min(g + 3, g1 - 1);
+      load_group(prs, bov, sov, sel_of(gb), ssel_of(gb), voff, soff, B);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(g, A);
+    if (g + 1 < g1) compute(g + 1, B);
   }
 }
 
