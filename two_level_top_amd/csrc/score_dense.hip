@@ -130,8 +130,6 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const Pair
     const int64_t pg = __builtin_amdgcn_readlane(pid, min(i, npg - 1));
     load_page(buffer_rsrc(pool + pg * kPageBytes, kPageBytes), voff, soff, o);
   };
-  // per-lane store offsets: score of position l of a page; key of block l / 8
-  // from lanes 8j (the others get an offset past every resource: dropped)
   // the rows' output pointers and bounds, as scalars (the compiler would
   // otherwise keep some in vector registers and build the store resources
   // lane by lane)
@@ -139,6 +137,8 @@ __device__ __forceinline__ void score_rows(const RowFrag<HB> (&f)[2], const Pair
   float* const Ku[2] = {uniform_ptr(Krow[0]), uniform_ptr(Krow[NR - 1])};
   const int lu[2] = {uniform(lens[0]), uniform(lens[NR - 1])};
   const int nbu[2] = {uniform(nblk[0]), uniform(nblk[NR - 1])};
+  // per-lane store offsets: score of position l of a page; key of block l / 8
+  // from lanes 8j (the others get an offset past every resource: dropped)
   const uint32_t soffs = (uint32_t)lane * 4u;
   const uint32_t koffs = (lane & 7) == 0 ? (uint32_t)(lane >> 3) * 4u : 0x80000000u;
   auto compute = [&](int i, const PageOps& cur) {
