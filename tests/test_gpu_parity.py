@@ -648,6 +648,10 @@ SPARSE_CASES = [
     (1700, 320, 4000, 64),    # 4 units per wave over 5-unit rows: waves span rows
     (640, 832, 8000, 64),     # 4 units per wave over 13-unit rows: waves span rows
     (8193, 256, 3000, 64),    # one run of 4 units per row, run-major; the last workgroup's spare waves
+    # kb not a multiple of 4 (the source's own k + 1 blocks): the flat expansion, 4 candidates a
+    # thread straddling rows
+    (1000, 513, 9000, 64),    # 4 units per wave over 9-unit rows: waves span rows
+    (70, 33, 1100, 8),        # split 8, one 33-block unit per row
 ]
 
 
@@ -680,10 +684,18 @@ def test_sparse_scores_every_launch_shape(idx, rows, kb, ctx, heads):
     phys_o, valid_o = oracle.expand(blocks, n_kept, wl.lens, wl.req, wl.page_table)
     assert np.array_equal(host(ch.table.phys), phys_o)
     assert np.array_equal(host(ch.table.valid_len), valid_o)
+    assert np.array_equal(host(ch.table.len), wl.lens)
+    assert np.array_equal(host(ch.table.req), wl.req)
+    U = (kb + 63) // 64
+    sched = host(ch.table.schedule).view(np.int32)
+    assert sched[0] == rows * U
+    exp = np.stack([np.repeat(np.arange(rows), U),
+                    np.where(64 * np.tile(np.arange(U), rows) < np.repeat(n_kept, U),
+                             64 * np.tile(np.arange(U), rows), -1)], axis=1)
+    assert np.array_equal(sched[4:4 + 2 * rows * U].reshape(-1, 2), exp), "work list"
     T = torch.full((rows, kb * 8), float("nan"), dtype=torch.float32, device="cuda")
     idx.idx_score_sparse_paged(ch.queries[1], ch.kp, ch.table, T)
     Tg = host(T)
-    U = (kb + 63) // 64
     if mode[0] == "upw":
         # rows whose units start or end inside a wave's run of units
         edges = np.unique(np.arange(0, rows * U, mode[1]) // U)

@@ -78,6 +78,77 @@ __global__ __launch_bounds__(256) void expand_kernel(PoolArgs kp, const int32_t*
   }
 }
 
+// Tables whose kb is not a multiple of 4 (the source's own (k + 1)-block
+// table: 513 blocks) are expanded as one flat array of rows * kb candidates:
+// thread t takes candidates 4 t .. 4 t + 3 with one 16-byte load and store
+// (they may straddle two rows), and the owner of candidate (r, u) also
+// writes work-list entry (r, u) for u < U, the owner of (r, 0) the row's
+// valid_len, len and req.  Per row (256 candidates a workgroup) the 513-block
+// table took three workgroups, the last with one candidate: long chunk
+// 0.10-0.11 ms for it beside the first consumer's scores, 0.06-0.08 ms this
+// way (the chunk time within noise: the kernel runs on the side stream).
+__global__ __launch_bounds__(256) void expand_flat_kernel(PoolArgs kp, const int32_t* __restrict__ req,
+                                                          const int32_t* __restrict__ len, int rows, int kb,
+                                                          const int32_t* __restrict__ blocks,
+                                                          const int32_t* __restrict__ n_kept,
+                                                          int32_t* __restrict__ phys,
+                                                          int32_t* __restrict__ valid_len,
+                                                          int32_t* __restrict__ len_out,
+                                                          int32_t* __restrict__ req_out,
+                                                          int32_t* __restrict__ sched) {
+  const int64_t total = (int64_t)rows * kb;
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= total) return;
+  const int units = (kb + kUnitBlocks - 1) / kUnitBlocks;
+  const bool whole = e0 + 3 < total;
+  int b[4] = {0, 0, 0, 0};
+  if (whole) {
+    const int4 v = *reinterpret_cast<const int4*>(blocks + e0);
+    b[0] = v.x;
+    b[1] = v.y;
+    b[2] = v.z;
+    b[3] = v.w;
+  } else {
+    for (int q = 0; q < 4 && e0 + q < total; ++q) b[q] = blocks[e0 + q];
+  }
+  int row = (int)(e0 / kb);
+  int i = (int)(e0 - (int64_t)row * kb);
+  int o[4] = {-1, -1, -1, -1};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (e0 + q >= total) break;
+    if (i == kb) {
+      ++row;
+      i = 0;
+    }
+    const int nk = min(max(n_kept[row], 0), kb);
+    if (i < nk) {
+      const int32_t* pt = kp.page_table + (int64_t)clamp_req(req[row], kp.num_req) * kp.max_pages;
+      const int pi = min(max(b[q] / kBlocksPerPage, 0), kp.max_pages - 1);
+      o[q] = pt[pi] * kBlocksPerPage + b[q] % kBlocksPerPage;
+    }
+    if (i < units) {
+      const int64_t e = (int64_t)row * units + i;
+      sched[4 + 2 * e] = row;
+      sched[5 + 2 * e] = i * kUnitBlocks < nk ? i * kUnitBlocks : -1;
+    }
+    if (i == 0) {
+      const int L = len[row];
+      const int nblk = L > 0 ? (L + kBlock - 1) / kBlock : 0;
+      valid_len[row] = L > 0 ? kBlock * nk - (kBlock * nblk - L) : 0;
+      len_out[row] = L;
+      req_out[row] = req[row];
+      if (row == 0) sched[0] = rows * units;
+    }
+    ++i;
+  }
+  if (whole) {
+    *reinterpret_cast<int4*>(phys + e0) = make_int4(o[0], o[1], o[2], o[3]);
+  } else {
+    for (int q = 0; q < 4 && e0 + q < total; ++q) phys[e0 + q] = o[q];
+  }
+}
+
 // entries of rows [0, rows): one thread per entry
 __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict__ n_kept, int rows,
                                                        int kb, int32_t* __restrict__ sched) {
@@ -199,13 +270,21 @@ hipError_t launch_expand(const PoolArgs& kp, const int32_t* req, const int32_t* 
                          int32_t* valid_len, int32_t* len_out, int32_t* req_out, void* schedule,
                          hipStream_t st) {
   if (rows <= 0) return launch_schedule(n_kept, 0, kb, schedule, st);
-  const bool vec = kb % 4 == 0 && reinterpret_cast<uintptr_t>(blocks) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(phys) % 16 == 0;
+  const bool aligned16 = reinterpret_cast<uintptr_t>(blocks) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(phys) % 16 == 0;
+  const bool vec = kb % 4 == 0 && aligned16;
+  int32_t* sched = static_cast<int32_t*>(schedule);
+  if (!vec && aligned16) {
+    const int64_t grid = ((int64_t)rows * kb + 1023) / 1024;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(expand_flat_kernel, dim3((unsigned)grid), dim3(256), 0, st, kp, req, len, rows, kb,
+                       blocks, n_kept, phys, valid_len, len_out, req_out, sched);
+    return hipGetLastError();
+  }
   const int per_wg = vec ? 1024 : 256;
   const int chunks = (kb + per_wg - 1) / per_wg;
   const int64_t grid = (int64_t)rows * chunks;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  int32_t* sched = static_cast<int32_t*>(schedule);
   if (vec)
     hipLaunchKernelGGL(expand_kernel<4>, dim3((unsigned)grid), dim3(256), 0, st, kp, req, len, rows, kb,
                        blocks, n_kept, phys, valid_len, len_out, req_out, sched, chunks);
