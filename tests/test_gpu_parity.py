@@ -917,6 +917,56 @@ def test_chunk_long_dense_source(idx):
     _check_chunk(wl, ch, np.array([0, 7, 9000, 16383]), 1)
 
 
+def test_dense_keys_newest_block_edges(idx):
+    """4096-position chunks (1024 rows x 64K context) with row lengths that put
+    the newest block at every offset of a page and next to page and chunk
+    edges, rows of a wave from one request and from two: the fused keys equal
+    idx_amax8_varlen on the same S for every row, the newest block's key is
+    +inf and nothing is written past it, the keys-only pass writes the same
+    keys, and S is within tolerance of the oracle on rows at the edges."""
+    from two_level_top_amd.chunk import Chunk
+    deltas = [-4097, -4096, -4095, -65, -64, -63, -9, -8, -7, -1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9,
+              63, 64, 65, 4095]
+    per = [301, 256, 467]   # odd counts: some waves hold rows of two requests
+    ctx = 65536
+    lens, r = [], 0
+    for n in per:
+        L = []
+        for _ in range(n):
+            base = 4096 * (1 + (r // len(deltas)) % 15)
+            L.append(int(min(max(base + deltas[r % len(deltas)], 1), ctx)))
+            r += 1
+        lens.append(L)
+    wl = workloads.custom("newest_edges", 91, 64, 64, 32, [ctx] * len(per), per, lens, n_layers=1)
+    say(f"dense keys, newest-block edges: {wl.rows} rows x {ctx}")
+    ch = Chunk(wl, n_consumers=0)
+    L0 = wl.layers[0]
+    q = idx.Query(dev(L0.qv), dev(L0.qs), dev(L0.w))
+    S = torch.full((wl.rows, wl.ld), float("nan"), dtype=torch.float32, device="cuda")
+    keys = torch.full((wl.rows, wl.ldk), -7.0, dtype=torch.float32, device="cuda")
+    idx.idx_score_dense_keys(q, ch.kp, ch.rows, S, keys, skip_le_blocks=0)
+    ref_keys = torch.full_like(keys, -7.0)
+    idx.idx_amax8_varlen(S, ch.rows.len, ref_keys, skip_le_blocks=0)
+    k2 = torch.full_like(keys, -7.0)
+    idx.idx_score_dense_keys(q, ch.kp, ch.rows, None, k2, skip_le_blocks=0, ld=wl.ld)
+    torch.cuda.synchronize()
+    assert bool((keys == ref_keys).all()), "fused keys differ from idx_amax8_varlen on the same S"
+    assert bool((keys == k2).all()), "keys-only pass differs from the pass that writes S"
+    kg = host(keys)
+    nblk = oracle.nblocks(wl.lens)
+    for i in range(wl.rows):
+        m = int(nblk[i])
+        assert np.isposinf(kg[i, m - 1]), f"row {i}: newest block key is not +inf"
+        assert np.isfinite(kg[i, :m - 1]).all(), f"row {i}: a key before the newest is not finite"
+        assert (kg[i, m:] == -7.0).all(), f"row {i}: keys written past nblk"
+    rows = np.array([0, 1, 2, 300, 301, 302, 556, 557, 1022, 1023] +
+                    [i for i in range(24, 36)])
+    ref = oracle.dense_scores(L0.qv, L0.qs, L0.w, wl.req, wl.lens, wl.pool, wl.page_table,
+                              row_ids=rows, ld=wl.ld)
+    valid = np.arange(wl.ld)[None, :] < wl.lens[rows][:, None]
+    assert_close(host(S[torch.from_numpy(rows).cuda()]), ref, valid, "newest-block edges dense")
+
+
 def test_keys_only_pass_matches_keys_with_scores(idx):
     """idx_score_dense_keys without S writes the same keys as with S."""
     from two_level_top_amd.chunk import Chunk
