@@ -58,6 +58,11 @@ def workload(name):
         return workloads.decode_mtp(), "decode MTP: 64 requests x 2 rows (len C-1, C), C U[4096,65536], H=64, kb=2048, 4 consumers, top-512"
     if name == "tiny":
         return workloads.tiny(), "tiny: 64 rows x 1024 context, H=8, kb=16, 2 consumers, top-32"
+    if name == "mixed":
+        wl = workloads.mixed()
+        return wl, (f"mixed: 8 prefill requests (rows log-U[128,4096], context log-U[8192,131072]) + "
+                    f"256 decode rows (context U[1024,262144]), {wl.rows} rows, H=64, kb=2048, 4 consumers, "
+                    f"top-512")
     raise SystemExit(f"unknown config {name}")
 
 
@@ -199,7 +204,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "decode_mtp", "tiny"])
+    ap.add_argument("--config", default="long", choices=["long", "prefill", "decode", "decode_mtp", "tiny", "mixed"])
     ap.add_argument("--cpu-rows", type=int, default=256,
                     help="rows of the CPU oracle sample (0 = skip the CPU baseline)")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
