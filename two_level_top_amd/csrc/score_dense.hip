@@ -239,15 +239,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   // Workgroup i runs on XCD i % 8.  Chunk c of row group g is workgroup
-  // g * nchunks + (c - (g / 16) % 8) mod nchunks: within 16 row groups each XCD
+  // g * nchunks + (c - (g / 64) % 8) mod nchunks: within 64 row groups each XCD
   // keeps one eighth of the chunks (its share of the K pool stays in its L2),
-  // and the eighth rotates every 16 row groups, so that a batch whose short
+  // and the eighth rotates every 64 row groups, so that a batch whose short
   // rows only fill the first chunks (the rest exit at once) spreads them over
   // all XCDs instead of the first few.  A mixed prefill + decode batch (9978
-  // rows, contexts 8K-262K): dense pass 5.45 -> 4.27 ms; the long chunk and
-  // prefill unchanged.
+  // rows, contexts 8K-262K): dense pass 5.45 -> 4.62 ms, the long chunk's
+  // time unchanged.  Rotating every 16 / 32 row groups gave 4.22 / 4.46 ms
+  // but, as the in-flight workgroups then span more rotations, 3.4 / 2.3 GB
+  // fetched by the long chunk's dense pass against 1.2 GB unrotated and
+  // 1.76 GB this way.
   const int rg = blockIdx.x / nchunks;
-  const int chunk = (int)((blockIdx.x % nchunks + (rg / 16) % 8) % nchunks);
+  const int chunk = (int)((blockIdx.x % nchunks + (rg / 64) % 8) % nchunks);
   const int r0 = (rg * kDenseWaves + wave) * kDenseRowsPerWave;
   if (r0 >= q.rows) return;
   const int r1 = r0 + 1 < q.rows ? r0 + 1 : -1;
